@@ -1,0 +1,299 @@
+"""Benchmark of one Veda block-sparse attention layer on one MI355X.
+
+A step is the whole hot path for one layer: veda_select (tile pooling +
+projection, pooled scores + per-segment top-k) followed by veda_sparse_attn
+(block-sparse attention over the selected tiles and the dense key ranges).
+Inputs are seeded synthetic tensors already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t2v5s]
+
+Prints one JSON line.  `value` is the dense-equivalent attention TFLOP/s of the
+whole step (4*B*H*Nq*Nk_all*d / (selector + attention time)).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dense-equiv attention TFLOP/s + selector+attn ms/layer at 90/95% sparsity"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t2v5s")
+    ap.add_argument("--also", default="mid", help="second workload reported beside (or 'none')")
+    ap.add_argument("--dense-reps", type=int, default=2)
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    return ap.parse_args()
+
+
+def attended_tokens_per_tile(wl, idx: np.ndarray) -> np.ndarray:
+    """Real key tokens each (b, h, query tile) attends to, from the index sets used."""
+    lens = []
+    for s in wl.segments:
+        T = wl.seg_tiles(s)
+        tl = np.full(T, wl.tile, dtype=np.int64)
+        tl[-1] = s.length - (T - 1) * wl.tile
+        lens.append(tl)
+    total = np.zeros(idx.shape[:-1], dtype=np.int64)
+    col = 0
+    for s, tl in zip(wl.segments, lens):
+        K = min(s.budget, wl.seg_tiles(s))
+        total += tl[idx[..., col:col + K]].sum(-1)
+        col += K
+    return total + sum(r.length for r in wl.dense)
+
+
+def query_rows_per_tile(wl) -> np.ndarray:
+    rows = np.full(wl.n_query_tiles, wl.tile, dtype=np.int64)
+    rows[-1] = wl.query.length - (wl.n_query_tiles - 1) * wl.tile
+    return rows
+
+
+class Layer:
+    """Device-resident inputs of one workload plus the calls of one step."""
+
+    def __init__(self, name):
+        import torch
+        from block_sparse_attention_predictor_amd import binding as B
+        from block_sparse_attention_predictor_amd import inputs as I
+        self.B = B
+        self.I = I
+        self.wl = wl = I.WORKLOADS[name]
+        self.q, self.k, self.v = I.make_qkv(wl)
+        self.w = I.make_weights(wl)
+        dev = torch.device("cuda:0")
+
+        def up(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.qd, self.kd, self.vd = up(self.q), up(self.k), up(self.v)
+        if self.w.fp8:
+            # load-time step: FP8 predictor -> bf16 on the GPU
+            self.wq = B.dequant_fp8_e4m3(torch.from_numpy(self.w.wq).to(dev), self.w.pow2_exp)
+            self.wk = B.dequant_fp8_e4m3(torch.from_numpy(self.w.wk).to(dev), self.w.pow2_exp)
+        else:
+            self.wq, self.wk = up(self.w.wq), up(self.w.wk)
+        self.L = B.layer_from_workload(wl)
+        self.dense = [(r.start, r.length) for r in wl.dense]
+        self.idx = torch.empty((wl.B, wl.H, wl.n_query_tiles, wl.k_total), dtype=torch.int32, device=dev)
+        self.ws = torch.empty(B.select_workspace_bytes(self.L) + 256, dtype=torch.uint8, device=dev)
+        self.out = torch.zeros_like(self.qd)
+        torch.cuda.synchronize()
+
+    def select(self):
+        self.B.select(self.L, self.qd, self.kd, self.wq, self.wk, workspace=self.ws, idx=self.idx)
+
+    def attn(self, idx=None, L=None):
+        self.B.sparse_attn(L or self.L, self.qd, self.kd, self.vd, self.idx if idx is None else idx,
+                           self.dense, out=self.out)
+
+    def step(self):
+        self.select()
+        self.attn()
+
+    def dense_flops(self):
+        wl = self.wl
+        nk_all = sum(s.length for s in wl.segments) + sum(r.length for r in wl.dense)
+        return 4.0 * wl.B * wl.H * wl.query.length * nk_all * wl.d
+
+    def actual_flops(self, idx_np):
+        per_tile = attended_tokens_per_tile(self.wl, idx_np)          # [B, H, Tq]
+        rows = query_rows_per_tile(self.wl)
+        return 4.0 * self.wl.d * float((per_tile * rows[None, None, :]).sum())
+
+    def full_layer(self):
+        full = self.I.with_full_budget(self.wl)
+        return self.B.layer_from_workload(full), full
+
+
+def time_events(fn, reps):
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    return float(np.mean(times)), float(np.min(times)), float(np.median(times))
+
+
+def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
+    import torch
+    lay = Layer(name)
+    wl = lay.wl
+    for _ in range(warmup):
+        lay.step()
+    torch.cuda.synchronize()
+    log(f"[{name}] timing {steps} steps")
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(steps):
+        lay.step()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = s.elapsed_time(e) / steps
+    # per-call times with events on the stream the kernels are launched on
+    sel_mean, sel_min, _ = time_events(lay.select, kernel_reps)
+    att_mean, att_min, _ = time_events(lay.attn, kernel_reps)
+    idx_np = lay.idx.cpu().numpy()
+    flops_actual = lay.actual_flops(idx_np)
+    flops_dense = lay.dense_flops()
+    res = {
+        "workload": name, "ms_per_step": ms_step, "wall_s": wall,
+        "selector_ms": sel_mean, "attn_ms": att_mean, "selector_ms_min": sel_min, "attn_ms_min": att_min,
+        "dense_equiv_tflops_step": flops_dense / (ms_step * 1e-3) / 1e12,
+        "dense_equiv_tflops_attn": flops_dense / (att_mean * 1e-3) / 1e12,
+        "actual_tflops_attn": flops_actual / (att_mean * 1e-3) / 1e12,
+        "actual_attn_tflop": flops_actual / 1e12, "dense_equiv_tflop": flops_dense / 1e12,
+        "sparsity_actual": 1.0 - flops_actual / flops_dense,
+    }
+    # pooling bandwidth: Q rows of the query segment + K rows of every key segment, once
+    pool_bytes = 2.0 * wl.B * wl.H * wl.d * (wl.query.length + sum(sg.length for sg in wl.segments))
+    res["pool_bytes"] = pool_bytes
+    if with_dense:
+        Lf, wlf = lay.full_layer()
+        idx_full = torch.from_numpy(lay.I.full_indices(wl)).to(lay.qd.device)
+        lay.attn(idx_full, Lf)
+        torch.cuda.synchronize()
+        log(f"[{name}] dense baseline (every tile selected)")
+        d_mean, d_min, _ = time_events(lambda: lay.attn(idx_full, Lf), dense_reps)
+        res["dense_ms"] = d_mean
+        res["dense_tflops"] = flops_dense / (d_mean * 1e-3) / 1e12
+        res["speedup_vs_dense"] = d_mean / ms_step
+        del idx_full
+    return lay, res
+
+
+def cpu_baseline(lay, log):
+    """The fp64 oracle on a bounded sample of the same layer, extrapolated to the layer."""
+    from oracle import veda_oracle as O
+    wl = lay.wl
+    segs = [(s.start, s.length, s.budget) for s in wl.segments]
+    query = (wl.query.start, wl.query.length)
+    heads = [0, wl.H - 1]
+    if lay.w.fp8:
+        wq = (lay.w.wq, lay.w.pow2_exp)
+        wk = (lay.w.wk, lay.w.pow2_exp)
+    else:
+        wq, wk = lay.w.wq, lay.w.wk
+    log("[cpu] oracle selection on 2 heads")
+    t0 = time.perf_counter()
+    idx_ref, _, _, _ = O.select(lay.q, lay.k, wq, wk, wl.tile, query, segs, heads=heads)
+    t_sel = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    tiles = sorted(set([0, wl.n_query_tiles - 1] + rng.integers(0, wl.n_query_tiles, 2).tolist()))
+    pairs = [(0, h, t) for h in heads for t in tiles]
+    log(f"[cpu] oracle attention on {len(pairs)} (head, tile) pairs")
+    t0 = time.perf_counter()
+    O.attend(lay.q, lay.k, lay.v, idx_ref, wl.tile, query, segs, [(r.start, r.length) for r in wl.dense],
+             pairs=pairs)
+    t_att = time.perf_counter() - t0
+    layer_s = t_sel * wl.H / len(heads) + t_att * (wl.B * wl.H * wl.n_query_tiles) / len(pairs)
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = min(threads, max(blas))
+    except Exception:  # pragma: no cover
+        pass
+    return {
+        "value": lay.dense_flops() / layer_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+        "cores": threads, "kind": "oracle",
+        "sample": (f"selection on heads {heads} (all {wl.n_query_tiles} query tiles) in {t_sel:.1f} s, "
+                   f"attention on {len(pairs)} (head, query tile) pairs in {t_att:.1f} s; "
+                   f"extrapolated to the {wl.H}-head layer: {layer_s:.0f} s per layer"),
+        "layer_s_extrapolated": layer_s,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path is not "
+                                   "sharded across GPUs (see DESIGN.md for how it would shard)"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    lay, res = measure(args.workload, args.steps, args.warmup, args.kernel_reps, args.dense_reps,
+                       not args.no_dense, log)
+    wl = lay.wl
+    also = None
+    if args.also and args.also != "none" and args.also != args.workload:
+        lay2, res2 = measure(args.also, args.steps, args.warmup, args.kernel_reps, args.dense_reps,
+                             not args.no_dense, log)
+        also = res2
+        del lay2
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(lay, log)
+    achieved = res["actual_tflops_attn"]
+    line = {
+        "metric": METRIC,
+        "value": round(res["dense_equiv_tflops_step"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": wl.B, "H": wl.H, "d": wl.d, "p": wl.p,
+                   "tile": wl.tile, "n_tokens": wl.n_tokens, "query_tokens": wl.query.length,
+                   "budgets": {s.name: s.budget for s in wl.segments},
+                   "dense_tokens": sum(r.length for r in wl.dense)},
+        "selector_ms": round(res["selector_ms"], 4),
+        "attn_ms": round(res["attn_ms"], 4),
+        "dense_equiv_tflops_attn": round(res["dense_equiv_tflops_attn"], 2),
+        "actual_tflops_attn": round(achieved, 2),
+        "mfma_util": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "dense_ms": round(res.get("dense_ms", float("nan")), 3) if "dense_ms" in res else None,
+        "speedup_vs_dense": round(res["speedup_vs_dense"], 2) if "speedup_vs_dense" in res else None,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "sparse_attn_kernel", "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
+        "cpu_baseline": cpu,
+        "also": also,
+        "detail": res,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+"""ctypes binding of libveda.so (declared in include/veda.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.  If
+the library has not been built, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libveda.so")
+
+MAX_SEGMENTS = 4
+MAX_DENSE = 8
+
+STATUS = {0: "VEDA_OK", -1: "VEDA_EINVAL", -2: "VEDA_EUNSUPPORTED", -3: "VEDA_EWORKSPACE",
+          -4: "VEDA_ERANGE", -5: "VEDA_ENOKEYS", -6: "VEDA_EHIP"}
+
+
+class VedaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class Range(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int64), ("len", ctypes.c_int64)]
+
+
+class Layer(ctypes.Structure):
+    """Mirror of veda_layer."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("p", ctypes.c_int32), ("tile", ctypes.c_int32), ("n_seg", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int64),
+        ("stride_b", ctypes.c_int64), ("stride_n", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("query", Range),
+        ("seg", Range * MAX_SEGMENTS),
+        ("budget", ctypes.c_int32 * MAX_SEGMENTS),
+    ]
+
+    @property
+    def Tq(self) -> int:
+        return -(-self.query.len // self.tile)
+
+    @property
+    def seg_tiles(self):
+        return [-(-self.seg[s].len // self.tile) for s in range(self.n_seg)]
+
+    @property
+    def Tk(self) -> int:
+        return sum(self.seg_tiles)
+
+    @property
+    def Ktot(self) -> int:
+        return sum(min(self.budget[s], t) for s, t in enumerate(self.seg_tiles))
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is missing: build it with "
+                           "`python -m block_sparse_attention_predictor_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(lib_path)
+    P = ctypes.c_void_p
+    L = ctypes.POINTER(Layer)
+    sig = {
+        "veda_abi_version": (ctypes.c_int, []),
+        "veda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "veda_k_total": (ctypes.c_int64, [L]),
+        "veda_layer_check": (ctypes.c_int, [L, ctypes.c_int]),
+        "veda_select_workspace_bytes": (ctypes.c_size_t, [L]),
+        "veda_pool_project": (ctypes.c_int, [L, P, P, P, P, P, P, P]),
+        "veda_score_topk": (ctypes.c_int, [L, P, P, P, P, P]),
+        "veda_select": (ctypes.c_int, [L, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "veda_sparse_attn": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+                                            ctypes.c_float, P, P, P]),
+        "veda_dequant_fp8_e4m3": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    return [n for n in ("veda_abi_version", "veda_status_string", "veda_k_total", "veda_layer_check",
+                        "veda_select_workspace_bytes", "veda_pool_project", "veda_score_topk",
+                        "veda_select", "veda_sparse_attn", "veda_dequant_fp8_e4m3")]
+
+
+def abi_version() -> int:
+    return _load().veda_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _load().veda_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise VedaError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------------------- layers
+
+def make_layer(*, B: int, H: int, d: int, p: int, tile: int, n_tokens: int,
+               query: Tuple[int, int], segments: Sequence[Tuple[int, int, int]],
+               strides: Tuple[int, int, int]) -> Layer:
+    """segments: [(start, length, budget), ...] in call order; strides in elements (b, n, h)."""
+    if len(segments) > MAX_SEGMENTS:
+        raise ValueError("too many key segments")
+    L = Layer()
+    L.B, L.H, L.d, L.p, L.tile = B, H, d, p, tile
+    L.n_seg = len(segments)
+    L.n_tokens = n_tokens
+    L.stride_b, L.stride_n, L.stride_h = strides
+    L.query.start, L.query.len = query
+    for s, (st, ln, bud) in enumerate(segments):
+        L.seg[s].start, L.seg[s].len = st, ln
+        L.budget[s] = bud
+    return L
+
+
+def strides_of(x: torch.Tensor) -> Tuple[int, int, int]:
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("expected a [B, N, H, d] tensor with a contiguous last dimension")
+    return x.stride(0), x.stride(1), x.stride(2)
+
+
+def layer_from_workload(wl, strides=None) -> Layer:
+    if strides is None:
+        strides = (wl.n_tokens * wl.H * wl.d, wl.H * wl.d, wl.d)
+    return make_layer(B=wl.B, H=wl.H, d=wl.d, p=wl.p, tile=wl.tile, n_tokens=wl.n_tokens,
+                      query=(wl.query.start, wl.query.length),
+                      segments=[(s.start, s.length, s.budget) for s in wl.segments],
+                      strides=strides)
+
+
+def dense_ranges(ranges: Sequence[Tuple[int, int]]):
+    arr = (Range * max(1, len(ranges)))()
+    for i, (st, ln) in enumerate(ranges):
+        arr[i].start, arr[i].len = st, ln
+    return arr, len(ranges)
+
+
+# ----------------------------------------------------------------------------- calls
+
+def _check_qkv(layer: Layer, *xs):
+    for x in xs:
+        if x.dtype != torch.bfloat16 or not x.is_cuda:
+            raise ValueError("Q/K/V must be bfloat16 device tensors")
+        if strides_of(x) != (layer.stride_b, layer.stride_n, layer.stride_h):
+            raise ValueError("tensor strides differ from the layer's strides")
+        if x.shape[0] != layer.B or x.shape[1] != layer.n_tokens or x.shape[2] != layer.H \
+                or x.shape[3] != layer.d:
+            raise ValueError("tensor shape differs from the layer")
+
+
+def select_workspace_bytes(layer: Layer) -> int:
+    return _load().veda_select_workspace_bytes(ctypes.byref(layer))
+
+
+def project(layer: Layer, q, k, wq, wk, stream=None):
+    """Pooled + projected vectors (q_hat [B,H,Tq,p], k_hat [B,H,Tk,p], fp32)."""
+    _check_qkv(layer, q, k)
+    dev = q.device
+    qh = torch.empty((layer.B, layer.H, layer.Tq, layer.p), dtype=torch.float32, device=dev)
+    kh = torch.empty((layer.B, layer.H, layer.Tk, layer.p), dtype=torch.float32, device=dev)
+    st = _load().veda_pool_project(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk),
+                                   _ptr(qh), _ptr(kh), _stream(stream))
+    _check(st, "veda_pool_project")
+    return qh, kh
+
+
+def score_topk(layer: Layer, q_hat, k_hat, want_scores: bool = False, stream=None):
+    dev = q_hat.device
+    idx = torch.empty((layer.B, layer.H, layer.Tq, layer.Ktot), dtype=torch.int32, device=dev)
+    sc = torch.empty((layer.B, layer.H, layer.Tq, layer.Tk), dtype=torch.float32, device=dev) \
+        if want_scores else None
+    st = _load().veda_score_topk(ctypes.byref(layer), _ptr(q_hat), _ptr(k_hat), _ptr(idx),
+                                 _ptr(sc), _stream(stream))
+    _check(st, "veda_score_topk")
+    return (idx, sc) if want_scores else idx
+
+
+def select(layer: Layer, q, k, wq, wk, want_scores: bool = False, workspace=None, idx=None,
+           stream=None):
+    """Tile indices int32 [B, H, Tq, Ktot] (and fp32 scores [B, H, Tq, Tk] if asked)."""
+    _check_qkv(layer, q, k)
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((layer.B, layer.H, layer.Tq, layer.Ktot), dtype=torch.int32, device=dev)
+    sc = torch.empty((layer.B, layer.H, layer.Tq, layer.Tk), dtype=torch.float32, device=dev) \
+        if want_scores else None
+    nbytes = select_workspace_bytes(layer)
+    if nbytes == 0:
+        _check(_load().veda_layer_check(ctypes.byref(layer), 1), "veda_select")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    st = _load().veda_select(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(idx),
+                             _ptr(sc), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "veda_select")
+    return (idx, sc) if want_scores else idx
+
+
+def sparse_attn(layer: Layer, q, k, v, idx, dense: Sequence[Tuple[int, int]] = (),
+                scale: float = 0.0, out=None, want_lse: bool = False, stream=None):
+    """Block-sparse attention; returns out (bf16, q's shape) [and lse fp32 [B, H, query.len]]."""
+    _check_qkv(layer, q, k, v)
+    if out is None:
+        out = torch.zeros_like(q)
+    else:
+        _check_qkv(layer, out)
+    lse = torch.empty((layer.B, layer.H, layer.query.len), dtype=torch.float32, device=q.device) \
+        if want_lse else None
+    if idx is not None:
+        if idx.dtype != torch.int32 or not idx.is_contiguous() or \
+                tuple(idx.shape) != (layer.B, layer.H, layer.Tq, layer.Ktot):
+            raise ValueError("idx must be contiguous int32 [B, H, Tq, Ktot]")
+    arr, n = dense_ranges(list(dense))
+    st = _load().veda_sparse_attn(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), arr, n,
+                                  float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "veda_sparse_attn")
+    return (out, lse) if want_lse else out
+
+
+def dequant_fp8_e4m3(codes: torch.Tensor, pow2_exp: int = 0, stream=None) -> torch.Tensor:
+    """E4M3FN bytes (uint8 device tensor) -> bf16 tensor of the same shape, exact."""
+    if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous uint8 device tensor")
+    dst = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device)
+    st = _load().veda_dequant_fp8_e4m3(_ptr(codes), _ptr(dst), codes.numel(), int(pow2_exp),
+                                       _stream(stream))
+    _check(st, "veda_dequant_fp8_e4m3")
+    return dst

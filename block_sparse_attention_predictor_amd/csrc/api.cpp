@@ -1,0 +1,233 @@
+// Host side of the C ABI: validation (complete before any device call), derived
+// layer geometry, workspace carving and kernel launches.
+#include "../../include/veda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "common.h"
+
+namespace {
+
+using veda::LayerDev;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool inside(const veda_range& r, int64_t n) {
+  return r.start >= 0 && r.len >= 0 && r.start <= n && r.len <= n - r.start;
+}
+
+bool overlap(const veda_range& a, const veda_range& b) {
+  if (a.len == 0 || b.len == 0) return false;
+  return a.start < b.start + b.len && b.start < a.start + a.len;
+}
+
+// Checks shared by every entry point that takes a layer.
+int check_layer(const veda_layer* L, bool for_select) {
+  if (!L) return VEDA_EINVAL;
+  if (L->B < 1 || L->H < 1 || L->n_tokens < 1) return VEDA_EINVAL;
+  if (L->d != 64 && L->d != 128) return VEDA_EUNSUPPORTED;
+  if (L->tile != 64 && L->tile != 128) return VEDA_EUNSUPPORTED;
+  if (for_select && (L->p < 16 || L->p > 256 || (L->p % 16) != 0)) return VEDA_EUNSUPPORTED;
+  if (L->n_seg < 0 || L->n_seg > VEDA_MAX_SEGMENTS) return VEDA_EUNSUPPORTED;
+  if (for_select && L->n_seg < 1) return VEDA_EINVAL;
+  if (L->stride_n <= 0 || L->stride_h <= 0 || L->stride_b < 0) return VEDA_EINVAL;
+  if ((L->stride_b % 8) || (L->stride_n % 8) || (L->stride_h % 8)) return VEDA_EINVAL;
+  if (L->stride_h < L->d) return VEDA_EINVAL;
+  if (!inside(L->query, L->n_tokens)) return VEDA_ERANGE;
+  int64_t tk = 0;
+  for (int s = 0; s < L->n_seg; ++s) {
+    if (L->seg[s].len < 1) return VEDA_EINVAL;
+    if (!inside(L->seg[s], L->n_tokens)) return VEDA_ERANGE;
+    if (L->budget[s] < 0) return VEDA_EINVAL;
+    for (int t = 0; t < s; ++t)
+      if (overlap(L->seg[s], L->seg[t])) return VEDA_ERANGE;
+    tk += ceil_div(L->seg[s].len, L->tile);
+  }
+  if (for_select && tk > VEDA_MAX_KEY_TILES) return VEDA_EUNSUPPORTED;
+  // index offsets are int32 inside the kernels
+  if ((int64_t)L->B * L->H * ceil_div(L->query.len, L->tile) * std::max<int64_t>(tk, 1) >
+      (int64_t)1 << 40)
+    return VEDA_EUNSUPPORTED;
+  return VEDA_OK;
+}
+
+int64_t k_total(const veda_layer* L) {
+  int64_t k = 0;
+  for (int s = 0; s < L->n_seg; ++s)
+    k += std::min<int64_t>(L->budget[s], ceil_div(L->seg[s].len, L->tile));
+  return k;
+}
+
+LayerDev to_dev(const veda_layer* L) {
+  LayerDev D{};
+  D.B = L->B;
+  D.H = L->H;
+  D.d = L->d;
+  D.p = L->p;
+  D.tile = L->tile;
+  D.n_seg = L->n_seg;
+  D.Tq = (int32_t)ceil_div(L->query.len, L->tile);
+  D.sb = L->stride_b;
+  D.sn = L->stride_n;
+  D.sh = L->stride_h;
+  D.q0 = L->query.start;
+  D.qlen = L->query.len;
+  int32_t koff = 0, toff = 0;
+  for (int s = 0; s < L->n_seg; ++s) {
+    veda::SegDev& g = D.seg[s];
+    g.start = L->seg[s].start;
+    g.len = L->seg[s].len;
+    g.T = (int32_t)ceil_div(g.len, L->tile);
+    g.K = std::min<int32_t>(L->budget[s], g.T);
+    g.koff = koff;
+    g.toff = toff;
+    koff += g.K;
+    toff += g.T;
+  }
+  D.Tk = toff;
+  D.Ktot = koff;
+  return D;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t qhat_bytes(const LayerDev& D) { return round256((size_t)D.B * D.H * D.Tq * D.p * 4); }
+size_t khat_bytes(const LayerDev& D) { return round256((size_t)D.B * D.H * D.Tk * D.p * 4); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VEDA_OK : VEDA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int veda_abi_version(void) { return VEDA_ABI_VERSION; }
+
+const char* veda_status_string(int status) {
+  switch (status) {
+    case VEDA_OK: return "ok";
+    case VEDA_EINVAL: return "invalid argument (null pointer, bad size, alignment or stride)";
+    case VEDA_EUNSUPPORTED: return "unsupported configuration (d, tile, p or count limits)";
+    case VEDA_EWORKSPACE: return "workspace too small";
+    case VEDA_ERANGE: return "token range outside the sequence or overlapping ranges";
+    case VEDA_ENOKEYS: return "a query tile would attend to no key";
+    case VEDA_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int64_t veda_k_total(const veda_layer* layer) {
+  if (!layer || layer->tile <= 0 || layer->n_seg < 0 || layer->n_seg > VEDA_MAX_SEGMENTS) return -1;
+  return k_total(layer);
+}
+
+int veda_layer_check(const veda_layer* layer, int for_select) {
+  return check_layer(layer, for_select != 0);
+}
+
+size_t veda_select_workspace_bytes(const veda_layer* layer) {
+  if (check_layer(layer, true) != VEDA_OK) return 0;
+  LayerDev D = to_dev(layer);
+  return qhat_bytes(D) + khat_bytes(D);
+}
+
+int veda_pool_project(const veda_layer* layer, const void* q, const void* k, const void* wq,
+                      const void* wk, float* q_hat, float* k_hat, void* stream) {
+  int st = check_layer(layer, true);
+  if (st != VEDA_OK) return st;
+  if (!q || !k || !wq || !wk || !q_hat || !k_hat) return VEDA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(wq) || !aligned16(wk) || !aligned16(q_hat) ||
+      !aligned16(k_hat))
+    return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0 && D.Tk == 0) return VEDA_OK;
+  return hip_status(veda::launch_pool_project(D, q, k, wq, wk, q_hat, k_hat, (hipStream_t)stream));
+}
+
+int veda_score_topk(const veda_layer* layer, const float* q_hat, const float* k_hat, int32_t* idx,
+                    float* scores_opt, void* stream) {
+  int st = check_layer(layer, true);
+  if (st != VEDA_OK) return st;
+  if (!q_hat || !k_hat || !idx) return VEDA_EINVAL;
+  if (!aligned16(q_hat) || !aligned16(k_hat) || !aligned16(idx)) return VEDA_EINVAL;
+  if (scores_opt && !aligned16(scores_opt)) return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) return VEDA_OK;
+  return hip_status(veda::launch_score_topk(D, q_hat, k_hat, idx, scores_opt, (hipStream_t)stream));
+}
+
+int veda_select(const veda_layer* layer, const void* q, const void* k, const void* wq,
+                const void* wk, int32_t* idx, float* scores_opt, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = check_layer(layer, true);
+  if (st != VEDA_OK) return st;
+  if (!q || !k || !wq || !wk || !idx || !ws) return VEDA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return VEDA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(wq) || !aligned16(wk) || !aligned16(idx))
+    return VEDA_EINVAL;
+  if (scores_opt && !aligned16(scores_opt)) return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  if (ws_bytes < qhat_bytes(D) + khat_bytes(D)) return VEDA_EWORKSPACE;
+  if (D.Tq == 0) return VEDA_OK;
+  float* qh = static_cast<float*>(ws);
+  float* kh = reinterpret_cast<float*>(static_cast<char*>(ws) + qhat_bytes(D));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = veda::launch_pool_project(D, q, k, wq, wk, qh, kh, s);
+  if (e != hipSuccess) return VEDA_EHIP;
+  return hip_status(veda::launch_score_topk(D, qh, kh, idx, scores_opt, s));
+}
+
+int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
+                     const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
+                     void* out, float* lse_opt, void* stream) {
+  int st = check_layer(layer, false);
+  if (st != VEDA_OK) return st;
+  if (!q || !k || !v || !out) return VEDA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VEDA_EINVAL;
+  if (lse_opt && !aligned16(lse_opt)) return VEDA_EINVAL;
+  if (n_dense < 0) return VEDA_EINVAL;
+  if (n_dense > VEDA_MAX_DENSE) return VEDA_EUNSUPPORTED;
+  if (n_dense > 0 && !dense) return VEDA_EINVAL;
+  if (!(std::isfinite(scale)) || scale < 0.f) return VEDA_EINVAL;
+  int64_t dense_tokens = 0;
+  for (int i = 0; i < n_dense; ++i) {
+    if (dense[i].len < 0) return VEDA_EINVAL;
+    if (!inside(dense[i], layer->n_tokens)) return VEDA_ERANGE;
+    for (int s = 0; s < layer->n_seg; ++s)
+      if (overlap(dense[i], layer->seg[s])) return VEDA_ERANGE;
+    for (int j = 0; j < i; ++j)
+      if (overlap(dense[i], dense[j])) return VEDA_ERANGE;
+    dense_tokens += dense[i].len;
+  }
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) return VEDA_OK;
+  if (D.Ktot == 0 && dense_tokens == 0) return VEDA_ENOKEYS;
+  if (D.Ktot > 0 && !idx) return VEDA_EINVAL;
+  if (idx && !aligned16(idx)) return VEDA_EINVAL;
+  veda::DenseDev DD{};
+  for (int i = 0; i < n_dense; ++i) {
+    if (dense[i].len == 0) continue;
+    DD.r[DD.n].start = dense[i].start;
+    DD.r[DD.n].len = dense[i].len;
+    DD.n++;
+  }
+  if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
+  return hip_status(veda::launch_sparse_attn(D, DD, q, k, v, idx, scale, out, lse_opt,
+                                             (hipStream_t)stream));
+}
+
+int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,
+                          void* stream) {
+  if (n < 0) return VEDA_EINVAL;
+  if (n == 0) return VEDA_OK;
+  if (!src || !dst_bf16) return VEDA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(dst_bf16) & 1u) != 0) return VEDA_EINVAL;
+  if (pow2_exp < -24 || pow2_exp > 24) return VEDA_EUNSUPPORTED;
+  return hip_status(veda::launch_dequant_e4m3(src, dst_bf16, n, pow2_exp, (hipStream_t)stream));
+}
+
+}  // extern "C"

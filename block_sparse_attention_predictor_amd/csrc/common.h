@@ -1,0 +1,58 @@
+// Shared definitions of the gfx950 kernels and their host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace veda {
+
+// Segment of key tiles as the kernels see it (derived on the host from veda_layer).
+struct SegDev {
+  int64_t start;   // first token
+  int64_t len;     // tokens
+  int32_t T;       // tiles = ceil(len / tile)
+  int32_t K;       // selected tiles per query tile = min(budget, T)
+  int32_t koff;    // first index column of this segment's block in idx rows
+  int32_t toff;    // first column of this segment in the concatenated key-tile space
+};
+
+struct RangeDev {
+  int64_t start;
+  int64_t len;
+};
+
+struct LayerDev {
+  int32_t B, H, d, p, tile, n_seg;
+  int32_t Tq;      // query tiles
+  int32_t Tk;      // key tiles over all segments
+  int32_t Ktot;    // selected tiles per query tile over all segments
+  int32_t pad_;
+  int64_t sb, sn, sh;       // element strides of q, k, v, out
+  int64_t q0, qlen;         // query segment
+  SegDev seg[4];
+};
+
+constexpr int kMaxSeg = 4;
+constexpr int kMaxDense = 8;
+
+struct DenseDev {
+  int32_t n;
+  int32_t pad_;
+  RangeDev r[kMaxDense];
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_pool_project(const LayerDev& L, const void* q, const void* k, const void* wq,
+                               const void* wk, float* q_hat, float* k_hat, hipStream_t s);
+hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float* k_hat,
+                             int32_t* idx, float* scores, hipStream_t s);
+hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& D, const void* q, const void* k,
+                              const void* v, const int32_t* idx, float scale, void* out,
+                              float* lse, hipStream_t s);
+hipError_t launch_dequant_e4m3(const uint8_t* src, void* dst, int64_t n, int32_t pow2_exp,
+                               hipStream_t s);
+
+// Rows of the score block one selection workgroup handles for Tk key tiles.
+int score_rows_per_block(int Tk);
+
+}  // namespace veda

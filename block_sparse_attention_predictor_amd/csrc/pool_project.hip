@@ -1,0 +1,164 @@
+// Tile mean-pooling of Q and K fused with the per-head predictor projection.
+//
+// Affine launch article, "Training the Selector, Not the Generator": the
+// selector consists of query and key projections trained per layer ("How the
+// SN120 Competition Works" gives one tensor per layer and projection).  Each
+// projection is applied here to the mean of the token rows of one tile:
+//     x_hat[b, h, t, :] = W[h] (1/|tile t|) sum_{n in tile t} X[b, n, h, :]
+//
+// HBM-bound: every Q row of the query segment and every K row of the key
+// segments is read exactly once (2 * H * d bytes per token).  One workgroup
+// owns one tile and a group of 8 heads; its 256 threads stream the tile's rows
+// with 16-byte loads (d/8 lanes per head row, 8 heads side by side, so a wave
+// reads whole contiguous head rows), sum in fp32 registers, combine the
+// row-parallel partial sums through LDS, divide by the number of real tokens,
+// then apply W[h] (bf16, read through L2) with fp32 dot products.
+#include "common.h"
+
+namespace veda {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadsPerGroup = 8;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void pool_project_kernel(
+    LayerDev L, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk, float* __restrict__ q_hat,
+    float* __restrict__ k_hat) {
+  constexpr int TPR = D / 8;                               // lanes per head row
+  constexpr int RP = kThreads / (kHeadsPerGroup * TPR);    // token rows in flight per step
+  __shared__ float red[RP][kHeadsPerGroup * D];
+
+  const int job = blockIdx.x;
+  const int h0 = blockIdx.y * kHeadsPerGroup;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+
+  // which tile: query tiles first, then the key tiles of every segment in call order
+  const uint16_t* x;
+  const uint16_t* W;
+  float* out;
+  int64_t start, len;
+  int64_t row_out;   // tile index within q_hat or k_hat
+  int32_t T_out;
+  if (job < L.Tq) {
+    x = q;
+    W = wq;
+    out = q_hat;
+    start = L.q0 + (int64_t)job * L.tile;
+    len = min((int64_t)L.tile, L.qlen - (int64_t)job * L.tile);
+    row_out = job;
+    T_out = L.Tq;
+  } else {
+    const int j = job - L.Tq;
+    int s = 0;
+#pragma unroll
+    for (int t = 1; t < kMaxSeg; ++t)
+      if (t < L.n_seg && j >= L.seg[t].toff) s = t;
+    const int tl = j - L.seg[s].toff;
+    x = k;
+    W = wk;
+    out = k_hat;
+    start = L.seg[s].start + (int64_t)tl * L.tile;
+    len = min((int64_t)L.tile, L.seg[s].len - (int64_t)tl * L.tile);
+    row_out = j;
+    T_out = L.Tk;
+  }
+
+  const int hl = (tid / TPR) % kHeadsPerGroup;
+  const int r0 = tid / (TPR * kHeadsPerGroup);
+  const int c = (tid % TPR) * 8;
+  const int h = h0 + hl;
+  const bool hv = h < L.H;
+
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+
+  if (hv) {
+    const uint16_t* base = x + (int64_t)b * L.sb + start * L.sn + (int64_t)h * L.sh + c;
+    int64_t r = r0;
+    // four rows in flight per thread
+    for (; r + 3 * RP < len; r += 4 * RP) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (r + u * RP) * L.sn));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[0] += bf16lo(v[u].x); acc[1] += bf16hi(v[u].x);
+        acc[2] += bf16lo(v[u].y); acc[3] += bf16hi(v[u].y);
+        acc[4] += bf16lo(v[u].z); acc[5] += bf16hi(v[u].z);
+        acc[6] += bf16lo(v[u].w); acc[7] += bf16hi(v[u].w);
+      }
+    }
+    for (; r < len; r += RP) {
+      u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + r * L.sn));
+      acc[0] += bf16lo(v.x); acc[1] += bf16hi(v.x);
+      acc[2] += bf16lo(v.y); acc[3] += bf16hi(v.y);
+      acc[4] += bf16lo(v.z); acc[5] += bf16hi(v.z);
+      acc[6] += bf16lo(v.w); acc[7] += bf16hi(v.w);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[r0][hl * D + c + e] = acc[e];
+  __syncthreads();
+  // combine the row-parallel partial sums; mean over the real tokens
+  const float inv_len = 1.0f / (float)len;
+  for (int i = tid; i < kHeadsPerGroup * D; i += kThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < RP; ++rr) s += red[rr][i];
+    red[0][i] = s * inv_len;
+  }
+  __syncthreads();
+
+  // projection: x_hat[h, o] = sum_c W[h, o, c] * mean[h, c]
+  const int P = L.p;
+  for (int o = tid; o < kHeadsPerGroup * P; o += kThreads) {
+    const int ohl = o / P;
+    const int oc = o - ohl * P;
+    const int oh = h0 + ohl;
+    if (oh >= L.H) continue;
+    const uint4* wrow = reinterpret_cast<const uint4*>(W + ((int64_t)oh * P + oc) * D);
+    const float* m = &red[0][ohl * D];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll 4
+    for (int cc = 0; cc < D / 8; ++cc) {
+      const uint4 w = wrow[cc];
+      const float* mm = m + cc * 8;
+      s0 = fmaf(bf16lo(w.x), mm[0], s0); s1 = fmaf(bf16hi(w.x), mm[1], s1);
+      s0 = fmaf(bf16lo(w.y), mm[2], s0); s1 = fmaf(bf16hi(w.y), mm[3], s1);
+      s0 = fmaf(bf16lo(w.z), mm[4], s0); s1 = fmaf(bf16hi(w.z), mm[5], s1);
+      s0 = fmaf(bf16lo(w.w), mm[6], s0); s1 = fmaf(bf16hi(w.w), mm[7], s1);
+    }
+    out[(((int64_t)b * L.H + oh) * T_out + row_out) * P + oc] = s0 + s1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool_project(const LayerDev& L, const void* q, const void* k, const void* wq,
+                               const void* wk, float* q_hat, float* k_hat, hipStream_t s) {
+  dim3 grid((unsigned)(L.Tq + L.Tk), (unsigned)((L.H + kHeadsPerGroup - 1) / kHeadsPerGroup),
+            (unsigned)L.B);
+  auto qq = static_cast<const uint16_t*>(q);
+  auto kk = static_cast<const uint16_t*>(k);
+  auto wqq = static_cast<const uint16_t*>(wq);
+  auto wkk = static_cast<const uint16_t*>(wk);
+  if (L.d == 128)
+    hipLaunchKernelGGL(pool_project_kernel<128>, grid, dim3(kThreads), 0, s, L, qq, kk, wqq, wkk,
+                       q_hat, k_hat);
+  else
+    hipLaunchKernelGGL(pool_project_kernel<64>, grid, dim3(kThreads), 0, s, L, qq, kk, wqq, wkk,
+                       q_hat, k_hat);
+  return hipGetLastError();
+}
+
+}  // namespace veda

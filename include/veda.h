@@ -1,0 +1,177 @@
+/*
+ * veda.h -- C ABI of the MI355X (gfx950) Veda-style block-sparse attention library.
+ *
+ * One attention layer of a video diffusion transformer, split as the method
+ * splits it:
+ *   selection  (a lightweight predictor, "Training the Selector, Not the
+ *              Generator" in the Affine launch article: the selector's query and
+ *              key projections pick which attention blocks are computed), and
+ *   attention  over the selected key tiles plus key ranges that stay dense
+ *              (Veda R2VA record, first paragraph: reference and current-video
+ *              tiles are chosen independently with fixed budgets per query tile
+ *              and head; text, VLM conditioning and audio attention stay dense).
+ *
+ * Conventions shared by every entry point
+ *   - Every buffer is caller-owned device memory (hipMalloc'd or torch-allocated).
+ *     The library never allocates or frees device memory, keeps no pointer after
+ *     a call returns and has no mutable global state: calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     work is enqueued asynchronously on it; nothing is synchronised.  A device
+ *     fault surfaces at the caller's next synchronisation.
+ *   - Arguments are validated completely on the host before any device call; an
+ *     invalid call returns a negative veda_status and enqueues nothing.
+ *   - Q, K, V and the attention output are bfloat16 tensors addressed as
+ *       elem(b, n, h, c) = base + b*stride_b + n*stride_n + h*stride_h + c
+ *     (strides in elements, the head dimension c contiguous).  The natural
+ *     layout is [B, n_tokens, H, d] contiguous.  Base pointers must be 16-byte
+ *     aligned and the three strides multiples of 8 elements.
+ *   - Tiles: the query segment is cut into Tq = ceil(query.len / tile) tiles
+ *     starting at query.start; key segment s into T_s = ceil(seg[s].len / tile)
+ *     tiles starting at seg[s].start.  The last tile of a segment may be partial.
+ */
+#ifndef VEDA_H
+#define VEDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VEDA_ABI_VERSION 1
+#define VEDA_MAX_SEGMENTS 4
+#define VEDA_MAX_DENSE 8
+#define VEDA_MAX_KEY_TILES 8192   /* sum over segments of T_s accepted by selection */
+
+typedef enum veda_status {
+  VEDA_OK = 0,
+  VEDA_EINVAL = -1,        /* null pointer, non-positive size, misaligned pointer or stride */
+  VEDA_EUNSUPPORTED = -2,  /* d not in {64,128}, tile not in {64,128}, p not a multiple of 16
+                              in [16, 256], more than VEDA_MAX_SEGMENTS / VEDA_MAX_DENSE,
+                              or more than VEDA_MAX_KEY_TILES key tiles */
+  VEDA_EWORKSPACE = -3,    /* workspace smaller than veda_select_workspace_bytes() */
+  VEDA_ERANGE = -4,        /* a range leaves [0, n_tokens), key segments overlap each other,
+                              or a dense range overlaps a key segment or another dense range */
+  VEDA_ENOKEYS = -5,       /* a query tile would attend to no key at all */
+  VEDA_EHIP = -6           /* the HIP runtime reported an error at launch */
+} veda_status;
+
+/* Token range [start, start + len). */
+typedef struct veda_range {
+  int64_t start;
+  int64_t len;
+} veda_range;
+
+/* Shape of one attention layer. */
+typedef struct veda_layer {
+  int32_t B;          /* batch                                                   */
+  int32_t H;          /* heads (K/V have as many heads as Q)                      */
+  int32_t d;          /* head dimension: 64 or 128                                */
+  int32_t p;          /* predictor dimension (rows of Wq[h], Wk[h]); selection only */
+  int32_t tile;       /* tokens per tile: 64 or 128                               */
+  int32_t n_seg;      /* key segments, 1..VEDA_MAX_SEGMENTS (0 allowed for attention
+                         when dense ranges exist)                                 */
+  int64_t n_tokens;   /* sequence length of Q, K, V                               */
+  int64_t stride_b, stride_n, stride_h;   /* element strides of Q, K, V and out  */
+  veda_range query;   /* the sparse query segment (generated video)               */
+  veda_range seg[VEDA_MAX_SEGMENTS];      /* key segments, in call order          */
+  int32_t budget[VEDA_MAX_SEGMENTS];      /* top-k budget per segment, >= 0; a budget
+                                             above T_s selects every tile          */
+} veda_layer;
+
+/* Ktot = sum_s min(budget[s], T_s): index entries per (b, h, query tile). */
+int64_t veda_k_total(const veda_layer* layer);
+
+/* Library ABI version (VEDA_ABI_VERSION of the build). */
+int veda_abi_version(void);
+
+/* Static text for a veda_status value. */
+const char* veda_status_string(int status);
+
+/* Host-only check of a layer description for selection (checks p) or for
+ * attention only (for_select = 0).  Returns VEDA_OK or the error code the
+ * corresponding entry point would return for this layer.  No device call. */
+int veda_layer_check(const veda_layer* layer, int for_select);
+
+/* Bytes of workspace veda_select needs: the projected pooled vectors
+ * q_hat [B,H,Tq,p] and k_hat [B,H,sum T_s,p] in fp32, 256-byte aligned.
+ * Returns 0 for an invalid layer. */
+size_t veda_select_workspace_bytes(const veda_layer* layer);
+
+/*
+ * Pool and project (steps a1 + a2).
+ * For every (b, h) and tile i of the query segment:
+ *     q_bar[i] = mean of Q[b, n, h, :] over the real tokens n of tile i (fp32 sums),
+ *     q_hat[b, h, i, :] = Wq[h] q_bar[i]      (Wq[h] is p x d, row-major, no bias);
+ * likewise k_hat[b, h, j, :] = Wk[h] k_bar[j] for every tile j of every key
+ * segment, segments concatenated in call order.
+ *   q, k   : bf16, strided as described above
+ *   wq, wk : bf16 [H, p, d] contiguous, 16-byte aligned
+ *   q_hat  : fp32 [B, H, Tq, p] contiguous (output)
+ *   k_hat  : fp32 [B, H, sum_s T_s, p] contiguous (output)
+ */
+int veda_pool_project(const veda_layer* layer, const void* q, const void* k,
+                      const void* wq, const void* wk, float* q_hat, float* k_hat,
+                      void* stream);
+
+/*
+ * Score and select (steps a3 + a4), from veda_pool_project's outputs.
+ *     S[b, h, i, j] = <q_hat[b,h,i,:], k_hat[b,h,j,:]>    (unscaled)
+ * For every (b, h, i) and segment s, the min(budget[s], T_s) tiles of segment s
+ * with the largest S; equal scores go to the lower tile index (-0 equals +0).
+ * They are written ascending, as segment-local tile ids, segment blocks in call
+ * order:  idx int32 [B, H, Tq, Ktot] contiguous (output).
+ *   scores_opt : NULL, or fp32 [B, H, Tq, sum_s T_s] contiguous receiving S.
+ * S is computed on bf16 matrix cores with each fp32 operand split into a high
+ * and a low bf16 part (three products), fp32 accumulation.
+ */
+int veda_score_topk(const veda_layer* layer, const float* q_hat, const float* k_hat,
+                    int32_t* idx, float* scores_opt, void* stream);
+
+/*
+ * Full selection: veda_pool_project into the workspace, then veda_score_topk.
+ *   ws, ws_bytes : device workspace of at least veda_select_workspace_bytes(layer),
+ *                  256-byte aligned.  Its contents are scratch.
+ */
+int veda_select(const veda_layer* layer, const void* q, const void* k,
+                const void* wq, const void* wk, int32_t* idx, float* scores_opt,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention (step a5).  For every (b, h) and query tile i, the key
+ * set A(b,h,i) is the union of the tokens of the tiles idx[b,h,i,:] selects
+ * (segment-local ids, segment blocks in call order, as veda_score_topk writes
+ * them) and of every dense range.  For each query row n of tile i:
+ *     out[b, n, h, :] = sum_{m in A} softmax_m(scale * <Q[b,n,h,:], K[b,m,h,:]>) V[b,m,h,:]
+ * computed with bf16 matrix cores, fp32 online softmax and fp32 accumulation,
+ * rounded to bf16 (nearest even).  Only the query segment's rows of `out` are
+ * written.
+ *   idx        : int32 [B, H, Tq, Ktot] contiguous.  Entries are NOT re-validated:
+ *                an id outside [0, T_s) is undefined behaviour.
+ *   dense      : host array of n_dense ranges (0 <= n_dense <= VEDA_MAX_DENSE),
+ *                disjoint from the key segments and from each other.
+ *   scale      : softmax scale; 0 selects 1/sqrt(d).
+ *   out        : bf16 with the same strides as q.
+ *   lse_opt    : NULL, or fp32 [B, H, query.len] receiving the natural-log
+ *                log-sum-exp of each row's scaled logits.
+ */
+int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
+                     const int32_t* idx, const veda_range* dense, int32_t n_dense,
+                     float scale, void* out, float* lse_opt, void* stream);
+
+/*
+ * FP8 predictor weights to bf16 at load (step a0; Veda R2VA record: the
+ * predictor is stored in FP8 and dequantised to BF16 at load).
+ *     dst[i] = E4M3FN(src[i]) * 2^pow2_exp, exactly representable in bf16.
+ * E4M3FN is the OCP FP8 format (bias 7, 3 mantissa bits, subnormals, max 448,
+ * S.1111.111 = NaN, no infinities); NaN codes produce a bf16 quiet NaN.
+ *   src : n bytes;  dst : n bf16 values (2-byte aligned);  -24 <= pow2_exp <= 24.
+ */
+int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VEDA_H */

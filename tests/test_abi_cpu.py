@@ -1,0 +1,148 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and
+its host-side validation returns the documented codes before any device call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_attention_predictor_amd import binding as Bnd
+from block_sparse_attention_predictor_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "veda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(Bnd.lib_path),
+                                reason="libveda.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(veda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(Bnd.lib_path)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", Bnd.lib_path], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s(veda_\w+)", out))
+    assert set(names) <= exported
+    assert set(Bnd.exported_symbols()) == set(names)
+
+
+def test_version_and_status_strings():
+    assert Bnd.abi_version() == 1
+    for code in range(-6, 1):
+        assert Bnd.status_string(code) and "unknown" not in Bnd.status_string(code)
+    assert "unknown" in Bnd.status_string(-99)
+
+
+def _layer(**kw):
+    wl = I.WORKLOADS["r2va"]
+    L = Bnd.layer_from_workload(wl)
+    for k, v in kw.items():
+        setattr(L, k, v)
+    return L
+
+
+def check(L, for_select=True):
+    return Bnd._load().veda_layer_check(ctypes.byref(L), 1 if for_select else 0)
+
+
+def test_valid_layers_pass_and_workspace_size():
+    for name in I.WORKLOAD_ORDER:
+        wl = I.WORKLOADS[name]
+        L = Bnd.layer_from_workload(wl)
+        assert check(L) == 0
+        assert L.Ktot == wl.k_total and L.Tk == wl.t_total
+        assert Bnd._load().veda_k_total(ctypes.byref(L)) == wl.k_total
+        ws = Bnd.select_workspace_bytes(L)
+        need = 4 * wl.H * wl.p * (wl.n_query_tiles + wl.t_total)
+        assert need <= ws <= need + 512
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d", 96, -2), ("d", 256, -2), ("tile", 32, -2), ("p", 24, -2), ("p", 0, -2), ("p", 512, -2),
+    ("B", 0, -1), ("H", 0, -1), ("n_tokens", 0, -1), ("n_seg", 5, -2), ("n_seg", 0, -1),
+    ("stride_n", 0, -1), ("stride_h", 4, -1), ("stride_n", 5124, -1),
+])
+def test_layer_errors(field, value, code):
+    assert check(_layer(**{field: value})) == code
+
+
+def test_range_errors():
+    L = _layer()
+    L.query.start = L.n_tokens - 10              # query runs past the sequence
+    assert check(L) == -4
+    L = _layer()
+    L.seg[0].start = 129000                      # reference overlaps the video segment
+    assert check(L) == -4
+    L = _layer()
+    L.budget[1] = -1
+    assert check(L) == -1
+    L = _layer()
+    L.seg[1].len = 0
+    assert check(L) == -1
+    # selection-only limits do not apply to attention
+    L = _layer(p=0)
+    assert check(L, for_select=False) == 0
+
+
+def test_entry_points_reject_before_device_calls():
+    lib = Bnd._load()
+    L = _layer()
+    fake = ctypes.c_void_p(0x10000)               # never dereferenced: validation fails first
+    # null pointers
+    assert lib.veda_select(ctypes.byref(L), None, fake, fake, fake, fake, None, fake, 1 << 40, None) == -1
+    assert lib.veda_pool_project(ctypes.byref(L), fake, None, fake, fake, fake, fake, None) == -1
+    assert lib.veda_score_topk(ctypes.byref(L), fake, fake, None, None, None) == -1
+    # misaligned pointer
+    odd = ctypes.c_void_p(0x10008)
+    assert lib.veda_pool_project(ctypes.byref(L), odd, fake, fake, fake, fake, fake, None) == -1
+    # workspace too small
+    need = Bnd.select_workspace_bytes(L)
+    assert lib.veda_select(ctypes.byref(L), fake, fake, fake, fake, fake, None, fake, need - 1, None) == -3
+    # misaligned workspace
+    assert lib.veda_select(ctypes.byref(L), fake, fake, fake, fake, fake, None, odd, need, None) == -1
+    # attention: dense range overlapping a key segment, dense ranges overlapping each other
+    arr, n = Bnd.dense_ranges([(133000, 100)])
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -4
+    arr, n = Bnd.dense_ranges([(133100, 100), (133150, 10)])
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -4
+    arr, n = Bnd.dense_ranges([(134800, 100)])  # past the end
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -4
+    # too many dense ranges
+    arr, n = Bnd.dense_ranges([(133056 + i, 1) for i in range(9)])
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -2
+    # no keys at all: every budget zero and no dense range
+    L0 = _layer()
+    L0.budget[0] = 0
+    L0.budget[1] = 0
+    arr, n = Bnd.dense_ranges([])
+    assert lib.veda_sparse_attn(ctypes.byref(L0), fake, fake, fake, None, arr, 0, 0.0, fake, None, None) == -5
+    # negative or non-finite scale
+    arr, n = Bnd.dense_ranges([])
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, 0, -1.0, fake, None, None) == -1
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, 0, float("nan"), fake, None, None) == -1
+    # dequant argument checks
+    assert lib.veda_dequant_fp8_e4m3(fake, fake, -1, 0, None) == -1
+    assert lib.veda_dequant_fp8_e4m3(None, fake, 8, 0, None) == -1
+    assert lib.veda_dequant_fp8_e4m3(fake, ctypes.c_void_p(0x10001), 8, 0, None) == -1
+    assert lib.veda_dequant_fp8_e4m3(fake, fake, 8, 30, None) == -2
+    assert lib.veda_dequant_fp8_e4m3(fake, fake, 0, 0, None) == 0      # empty: nothing to do
+
+
+def test_empty_query_segment_is_a_no_op():
+    lib = Bnd._load()
+    L = _layer()
+    L.query.len = 0
+    fake = ctypes.c_void_p(0x10000)
+    arr, n = Bnd.dense_ranges([])
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, 0, 0.0, fake, None, None) == 0
+    assert lib.veda_score_topk(ctypes.byref(L), fake, fake, fake, None, None) == 0
