@@ -8,42 +8,48 @@
 // One workgroup computes one (b, h, query tile); each of its tile/32 waves owns
 // 32 query rows.  Keys stream through LDS in blocks of 64 tokens: first the
 // tiles named by the index row (gathered by id), then every dense range, cut
-// into 64-token blocks.  The next block's K/V rows are loaded into registers
-// while the current block is multiplied, then written to LDS (K row-major, V
-// transposed), so HBM latency hides behind the matrix work.
+// into 64-token blocks.
+//
+// Memory path (gfx950):
+//  * K and V rows go HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per
+//    lane, no VGPR staging) into a two-stage ring; block n+1 is in flight while
+//    block n is multiplied, with one workgroup barrier per block.
+//  * Rows are stored unpadded with their 16-byte chunks XOR-swizzled by row, so
+//    the matrix-core operand reads below are free of LDS bank conflicts.
+//  * V stays row-major; the transposing LDS read (ds_read_b64_tr_b16) hands each
+//    lane four consecutive keys of one head-dimension column, which is exactly
+//    the V^T operand layout.
 //
 // Both products are computed transposed on v_mfma_f32_32x32x16_bf16:
 //     S^T (keys x queries)  = K . Q^T     A = K rows from LDS, B = Q^T held in VGPRs
-//     O^T (d x queries)    += V^T . P^T   A = V^T rows from LDS, B = P^T from S^T's accumulator
-// With this orientation every accumulator value a lane holds belongs to one
-// query row (lane % 32), so the online softmax needs a single cross-lane
-// exchange (lane ^ 32) per block for the running maximum, and P^T is formed
-// from S^T's accumulator registers without any shuffle: the key order inside
-// each 16-key slice of the O^T contraction is permuted to match the
-// accumulator layout, and V^T is stored in LDS in that same permuted order.
-// Softmax runs in fp32 in the exp2 domain; P is rounded to bf16 for the second
-// product; O is accumulated in fp32 and rounded to bf16 once at the end.
+//     O^T (d x queries)    += V^T . P^T   A = V^T via transposing reads, B = P^T
+// Every accumulator value a lane holds then belongs to one query row
+// (lane % 32): the online softmax needs one cross-lane exchange (lane ^ 32) per
+// block, and P^T is built from S^T's accumulator registers without a shuffle
+// (the key order inside each 16-key slice of the O^T contraction is permuted to
+// match the accumulator layout; the V^T reads use the same permutation).
+// Softmax is fp32 in the exp2 domain with a lazily updated running maximum: the
+// output is rescaled only when a block's maximum exceeds the running one by
+// more than 2^8, which leaves the result unchanged (numerator and denominator
+// share the stale maximum) and removes the per-block rescale in the common case.
+// P is rounded to bf16 for the second product; O accumulates in fp32 and is
+// rounded to bf16 once at the end.
 #include "common.h"
+
+#include <type_traits>
 
 namespace veda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
-constexpr int KB = 64;          // keys per block
-constexpr int VP = KB + 8;      // V^T row pitch in LDS (bf16): 144 B, conflict-free 16 B reads
-
-// position of key k (0..63) inside V^T's permuted row
-__device__ __forceinline__ int vt_pos(int k) {
-  const int kl = k & 15;
-  const int g = kl >> 2;
-  return (k & ~15) + (g & 1) * 8 + (g >> 1) * 4 + (kl & 3);
-}
-
-__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
-  return (uint32_t)a | ((uint32_t)b << 16);
-}
+constexpr int KB = 64;            // keys per block
+constexpr float kLazyRescale = 8.0f;
 
 struct Block {
   int64_t start;
@@ -86,19 +92,27 @@ __device__ __forceinline__ Block key_block(const LayerDev& L, const DenseDev& DN
   return blk;
 }
 
+// 16-byte chunk swizzles (CPR = chunks per row).
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) { return row & (CPR - 1); }
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) * (CPR / 4); }
+
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int NT = 64 * NW;                 // threads
   constexpr int CPR = D / 8;                  // 16-byte chunks per key row
-  constexpr int KPT = KB * CPR / NT;          // keys per thread in a block (2, 4 or 8)
-  constexpr int KP = D + 8;                   // K row pitch in LDS (bf16)
-  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "unsupported block split");
+  constexpr int SLOTS = KB * CPR;             // 16-byte slots per K (or V) block
+  constexpr int LPT = SLOTS / NT;             // DMA loads per thread per tensor and block
+  static_assert(SLOTS % NT == 0, "block split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[KB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KB * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -119,8 +133,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
   const int h = bh % L.H;
   const int b = bh / L.H;
 
-  const int64_t q_first = L.q0 + (int64_t)qt * L.tile;              // first row of the tile
-  const int64_t q_end = L.q0 + L.qlen;                              // end of the query segment
+  const int64_t q_first = L.q0 + (int64_t)qt * L.tile;
+  const int64_t q_end = L.q0 + L.qlen;
   const int64_t head_off = (int64_t)b * L.sb + (int64_t)h * L.sh;
   const int32_t* idx_row = idx ? idx + ((int64_t)bh * L.Tq + qt) * L.Ktot : nullptr;
 
@@ -143,25 +157,28 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
   for (int r = 0; r < DN.n; ++r) ndense_blocks += (int)((DN.r[r].len + KB - 1) / KB);
   const int nblk = nsel_blocks + ndense_blocks;
 
-  // ---- loader mapping: thread holds keys kg*KPT .. +KPT-1, d-chunk c
-  const int lc = (tid % CPR) * 8;
-  const int lkg = tid / CPR;
-  uint4 kr[KPT], vr[KPT];
-
-  auto load_block = [&](int bi) -> int {
-    const Block blk = key_block(L, DN, idx_row, nsel_blocks, bpt, bi);
-    const uint16_t* kb = k + head_off + blk.start * L.sn + lc;
-    const uint16_t* vb = v + head_off + blk.start * L.sn + lc;
+  // ---- DMA mapping: load i of this thread fills 16-byte slot (wave*LPT + i)*64 + lane
+  int dma_row[LPT], dma_col_k[LPT], dma_col_v[LPT];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int key = lkg * KPT + u;
-      if (key < blk.n) {
-        kr[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)key * L.sn);
-        vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)key * L.sn);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
+  for (int i = 0; i < LPT; ++i) {
+    const int s = (wave * LPT + i) * 64 + lane;
+    dma_row[i] = s / CPR;
+    const int pc = s % CPR;                      // physical chunk
+    dma_col_k[i] = (pc ^ swz_k<CPR>(dma_row[i])) * 8;
+    dma_col_v[i] = (pc ^ swz_v<CPR>(dma_row[i])) * 8;
+  }
+  auto issue = [&](int bi, uint16_t* kd, uint16_t* vd) -> int {
+    const Block blk = key_block(L, DN, idx_row, nsel_blocks, bpt, bi);
+    if (blk.n <= 0) return 0;
+    const uint16_t* kb = k + head_off + blk.start * L.sn;
+    const uint16_t* vb = v + head_off + blk.start * L.sn;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int64_t r = dma_row[i] < blk.n ? dma_row[i] : blk.n - 1;   // clamp past the end
+      char* lk = reinterpret_cast<char*>(kd) + (wave * LPT + i) * 1024;
+      char* lv = reinterpret_cast<char*>(vd) + (wave * LPT + i) * 1024;
+      __builtin_amdgcn_global_load_lds((void*)(kb + r * L.sn + dma_col_k[i]), (lds_void_t)lk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((void*)(vb + r * L.sn + dma_col_v[i]), (lds_void_t)lv, 16, 0, 0);
     }
     return blk.n;
   };
@@ -174,38 +191,27 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  int cur_n = nblk > 0 ? load_block(0) : 0;
-  for (int bi = 0; bi < nblk; ++bi) {
+  // per-lane operand addresses that do not depend on the block
+  // K (A of S^T): row mb*32 + l32, logical chunk 2*kk + hi
+  // V^T (A of O^T) via transposing reads: group G = lane/16, j = lane%16
+  const int vg2 = (lane >> 4) & 1;
+  const int vj = lane & 15;
+
+  // One block: wait for its DMA, barrier, start the next block's DMA into the other
+  // stage, then both products.  ST is the stage of this block (a compile-time
+  // constant, so every LDS access names its buffer statically).
+  int cur_n = nblk > 0 ? issue(0, Ks0, Vs0) : 0;
+  auto step = [&](auto stage, int bi) {
+    constexpr int ST = decltype(stage)::value;
+    uint16_t* Kc = ST ? Ks1 : Ks0;
+    uint16_t* Vc = ST ? Vs1 : Vs0;
     const int n = cur_n;
+    // this wave's DMA for block bi (the only loads in flight) has landed; the barrier
+    // then makes every wave's part visible and frees the other stage
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (n > 0) {
-      // K rows as they are
-#pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        *reinterpret_cast<uint4*>(&Ks[(lkg * KPT + u) * KP + lc]) = kr[u];
-      // V transposed, keys in the permuted order of the P^T operand
-      const uint16_t* vs = reinterpret_cast<const uint16_t*>(vr);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (KPT == 2) {
-          const int k0 = lkg * 2;
-          *reinterpret_cast<uint32_t*>(&Vt[(lc + e) * VP + vt_pos(k0)]) =
-              pack2(vs[0 * 8 + e], vs[1 * 8 + e]);
-        } else {
-#pragma unroll
-          for (int g4 = 0; g4 < KPT / 4; ++g4) {
-            const int k0 = lkg * KPT + g4 * 4;
-            uint2 w;
-            w.x = pack2(vs[(g4 * 4 + 0) * 8 + e], vs[(g4 * 4 + 1) * 8 + e]);
-            w.y = pack2(vs[(g4 * 4 + 2) * 8 + e], vs[(g4 * 4 + 3) * 8 + e]);
-            *reinterpret_cast<uint2*>(&Vt[(lc + e) * VP + vt_pos(k0)]) = w;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    if (bi + 1 < nblk) cur_n = load_block(bi + 1);
-    if (n <= 0) continue;
+    if (bi + 1 < nblk) cur_n = ST ? issue(bi + 1, Ks0, Vs0) : issue(bi + 1, Ks1, Vs1);
+    if (n <= 0) return;
 
     // ---- S^T = K Q^T for 64 keys: two 32-key halves
     f32x16 s[2];
@@ -213,10 +219,11 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
+      const int row = mb * 32 + l32;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&Ks[(mb * 32 + l32) * KP + kk * 16 + hi * 8]);
+        const int pc = (2 * kk + hi) ^ swz_k<CPR>(row);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kc[row * D + pc * 8]);
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[kk], s[mb], 0, 0, 0);
       }
     }
@@ -230,41 +237,58 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
           if (key >= n) s[mb][e] = -INFINITY;
         }
     }
-    // ---- online softmax, exp2 domain
+    // ---- online softmax, exp2 domain, lazy rescale
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    }
     bf16x8 pb[4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_new));
-        psum += pe;
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
+        l_run += pe;
         pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)pe;
       }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
 
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[(db * 32 + l32) * VP + c * 16 + hi * 8]);
+        s16x4 part[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = 16 * c + 8 * r + 4 * hi + (vj >> 2);
+          const int dcol = 32 * db + 16 * vg2 + 4 * (vj & 3);
+          const int pc = (dcol >> 3) ^ swz_v<CPR>(row);
+          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t)(&Vc[row * D + pc * 8 + (dcol & 7)]));
+        }
+        // the two halves as one 16-byte operand (whole-vector cast: building it
+        // element by element through bf16 scalars is lowered wrongly by the compiler)
+        const s16x8 both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, both);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], o[db], 0, 0, 0);
       }
     }
+  };
+  for (int bi = 0; bi < nblk; bi += 2) {
+    step(std::integral_constant<int, 0>{}, bi);
+    if (bi + 1 < nblk) step(std::integral_constant<int, 1>{}, bi + 1);
   }
 
   // ---- normalise and store
@@ -277,13 +301,13 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d0 = db * 32 + i * 8 + hi * 4;
-        uint2 w;
         const __bf16 o0 = (__bf16)(o[db][i * 4 + 0] * inv);
         const __bf16 o1 = (__bf16)(o[db][i * 4 + 1] * inv);
         const __bf16 o2 = (__bf16)(o[db][i * 4 + 2] * inv);
         const __bf16 o3 = (__bf16)(o[db][i * 4 + 3] * inv);
-        w.x = pack2(__builtin_bit_cast(uint16_t, o0), __builtin_bit_cast(uint16_t, o1));
-        w.y = pack2(__builtin_bit_cast(uint16_t, o2), __builtin_bit_cast(uint16_t, o3));
+        uint2 w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, o2) | ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
         *reinterpret_cast<uint2*>(op + d0) = w;
       }
     if (lse && hi == 0) {
