@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy first (byte-counter calibration)")
     return ap.parse_args()
 
 
@@ -138,6 +140,18 @@ def time_events(fn, reps):
     return float(np.mean(times)), float(np.min(times)), float(np.median(times))
 
 
+def copy_calibration():
+    """A plain device copy of known size (1 GiB read + 1 GiB written), run once so that
+    hardware byte counters can be scaled against it in a profiled run."""
+    import torch
+    n = 1 << 29                                   # bf16 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
     import torch
     lay = Layer(name)
@@ -146,20 +160,28 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
         lay.step()
     torch.cuda.synchronize()
     log(f"[{name}] timing {steps} steps")
+    # events on the stream the kernels are launched on (torch's current stream, which
+    # the binding passes to the library): e0 | select | e1 | attention | e2 per step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     s.record()
-    for _ in range(steps):
-        lay.step()
+    for i in range(steps):
+        ev[i][0].record()
+        lay.select()
+        ev[i][1].record()
+        lay.attn()
+        ev[i][2].record()
     e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = s.elapsed_time(e) / steps
-    # per-call times with events on the stream the kernels are launched on
-    sel_mean, sel_min, _ = time_events(lay.select, kernel_reps)
-    att_mean, att_min, _ = time_events(lay.attn, kernel_reps)
+    sel_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    att_ms = [b.elapsed_time(c) for _, b, c in ev]
+    sel_mean, sel_min = float(np.mean(sel_ms)), float(np.min(sel_ms))
+    att_mean, att_min = float(np.mean(att_ms)), float(np.min(att_ms))
     idx_np = lay.idx.cpu().numpy()
     flops_actual = lay.actual_flops(idx_np)
     flops_dense = lay.dense_flops()
@@ -189,30 +211,42 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
     return lay, res
 
 
-def cpu_baseline(lay, log):
-    """The fp64 oracle on a bounded sample of the same layer, extrapolated to the layer."""
+def cpu_baseline(lay, log, budget_s=20.0):
+    """The fp64 oracle on a bounded sample of the same layer (about budget_s of CPU
+    work), extrapolated to the whole layer."""
     from oracle import veda_oracle as O
     wl = lay.wl
     segs = [(s.start, s.length, s.budget) for s in wl.segments]
     query = (wl.query.start, wl.query.length)
-    heads = [0, wl.H - 1]
+    dense = [(r.start, r.length) for r in wl.dense]
     if lay.w.fp8:
         wq = (lay.w.wq, lay.w.pow2_exp)
         wk = (lay.w.wk, lay.w.pow2_exp)
     else:
         wq, wk = lay.w.wq, lay.w.wk
-    log("[cpu] oracle selection on 2 heads")
-    t0 = time.perf_counter()
-    idx_ref, _, _, _ = O.select(lay.q, lay.k, wq, wk, wl.tile, query, segs, heads=heads)
-    t_sel = time.perf_counter() - t0
+    # selection: heads one at a time until a third of the budget is used
+    heads, t_sel = [], 0.0
+    idx_ref = None
+    for h in range(wl.H):
+        log(f"[cpu] oracle selection, head {h}")
+        t0 = time.perf_counter()
+        r, _, _, _ = O.select(lay.q, lay.k, wq, wk, wl.tile, query, segs, heads=[h])
+        t_sel += time.perf_counter() - t0
+        idx_ref = r if idx_ref is None else idx_ref
+        idx_ref[:, h] = r[:, h]
+        heads.append(h)
+        if t_sel > budget_s / 3:
+            break
+    # attention: (head, tile) pairs of the selected heads until the budget is used
     rng = np.random.default_rng(0)
-    tiles = sorted(set([0, wl.n_query_tiles - 1] + rng.integers(0, wl.n_query_tiles, 2).tolist()))
-    pairs = [(0, h, t) for h in heads for t in tiles]
+    pairs, t_att = [], 0.0
+    while t_att < budget_s * 2 / 3 and len(pairs) < wl.H * wl.n_query_tiles:
+        pr = (0, int(rng.choice(heads)), int(rng.integers(0, wl.n_query_tiles)))
+        t0 = time.perf_counter()
+        O.attend(lay.q, lay.k, lay.v, idx_ref, wl.tile, query, segs, dense, pairs=[pr])
+        t_att += time.perf_counter() - t0
+        pairs.append(pr)
     log(f"[cpu] oracle attention on {len(pairs)} (head, tile) pairs")
-    t0 = time.perf_counter()
-    O.attend(lay.q, lay.k, lay.v, idx_ref, wl.tile, query, segs, [(r.start, r.length) for r in wl.dense],
-             pairs=pairs)
-    t_att = time.perf_counter() - t0
     layer_s = t_sel * wl.H / len(heads) + t_att * (wl.B * wl.H * wl.n_query_tiles) / len(pairs)
     threads = len(os.sched_getaffinity(0))
     try:
@@ -225,9 +259,9 @@ def cpu_baseline(lay, log):
     return {
         "value": lay.dense_flops() / layer_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
         "cores": threads, "kind": "oracle",
-        "sample": (f"selection on heads {heads} (all {wl.n_query_tiles} query tiles) in {t_sel:.1f} s, "
-                   f"attention on {len(pairs)} (head, query tile) pairs in {t_att:.1f} s; "
-                   f"extrapolated to the {wl.H}-head layer: {layer_s:.0f} s per layer"),
+        "sample": (f"selection on {len(heads)} of {wl.H} heads (all {wl.n_query_tiles} query tiles) in "
+                   f"{t_sel:.1f} s; attention on {len(pairs)} random (head, query tile) pairs in {t_att:.1f} s; "
+                   f"extrapolated to the whole layer: {layer_s:.0f} s per layer"),
         "layer_s_extrapolated": layer_s,
         "cpu": platform.processor() or platform.machine(),
     }
@@ -247,6 +281,8 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    if args.calib_copy:
+        copy_calibration()
     lay, res = measure(args.workload, args.steps, args.warmup, args.kernel_reps, args.dense_reps,
                        not args.no_dense, log)
     wl = lay.wl

@@ -42,55 +42,59 @@ namespace veda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+typedef const __attribute__((address_space(4))) int32_t* const_i32_t;
 
 constexpr int KB = 64;            // keys per block
 constexpr float kLazyRescale = 8.0f;
 
 struct Block {
   int64_t start;
-  int n;
+  int n;                          // 0 marks the end of the key list
 };
 
-// Key block `bi` of the current (b, h, query tile): selected tiles first (ids from
-// the index row, segment blocks in order), then the dense ranges.
-__device__ __forceinline__ Block key_block(const LayerDev& L, const DenseDev& DN,
-                                           const int32_t* __restrict__ idx_row, int nsel_blocks,
-                                           int bpt, int bi) {
-  Block blk;
-  if (bi < nsel_blocks) {
-    const int sel = bi / bpt;
-    const int sub = bi - sel * bpt;
-    int s = 0;
-#pragma unroll
-    for (int t = 1; t < kMaxSeg; ++t)
-      if (t < L.n_seg && sel >= L.seg[t].koff) s = t;
-    const int tile_id = __builtin_amdgcn_readfirstlane(idx_row[sel]);
-    const int64_t rel = (int64_t)tile_id * L.tile + (int64_t)sub * KB;
-    blk.start = L.seg[s].start + rel;
-    const int64_t rem = L.seg[s].len - rel;
-    blk.n = (int)(rem < KB ? (rem > 0 ? rem : 0) : KB);
-  } else {
-    int bd = bi - nsel_blocks;
-    blk.start = 0;
-    blk.n = 0;
-    for (int r = 0; r < DN.n; ++r) {
-      const int nb = (int)((DN.r[r].len + KB - 1) / KB);
-      if (bd < nb) {
-        blk.start = DN.r[r].start + (int64_t)bd * KB;
-        const int64_t rem = DN.r[r].len - (int64_t)bd * KB;
-        blk.n = (int)(rem < KB ? rem : KB);
-        break;
+// Walks the key blocks of one (b, h, query tile): the selected tiles of every
+// segment in index order (tiles longer than a block give several blocks; the
+// empty tail of a short last tile gives none), then every dense range.
+struct BlockIter {
+  int sel = 0, sub = 0, seg = 0, dr = 0;
+  int64_t doff = 0;
+
+  __device__ __forceinline__ Block next(const LayerDev& L, const DenseDev& DN, const_i32_t idx_row) {
+    const int bpt = L.tile / KB;
+    for (;;) {
+      if (sel < L.Ktot) {
+        while (sel >= L.seg[seg].koff + L.seg[seg].K) ++seg;
+        const int t = idx_row[sel];
+        const int64_t rel = (int64_t)t * L.tile + (int64_t)sub * KB;
+        const int64_t rem = L.seg[seg].len - rel;
+        const int64_t st = L.seg[seg].start + rel;
+        if (++sub == bpt) {
+          sub = 0;
+          ++sel;
+        }
+        if (rem > 0) return Block{st, (int)(rem < KB ? rem : KB)};
+        continue;
       }
-      bd -= nb;
+      if (dr < DN.n) {
+        const int64_t rem = DN.r[dr].len - doff;
+        const int64_t st = DN.r[dr].start + doff;
+        doff += KB;
+        if (doff >= DN.r[dr].len) {
+          ++dr;
+          doff = 0;
+        }
+        return Block{st, (int)(rem < KB ? rem : KB)};
+      }
+      return Block{0, 0};
     }
   }
-  return blk;
-}
+};
 
 // 16-byte chunk swizzles (CPR = chunks per row).
 template <int CPR>
@@ -109,34 +113,37 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   constexpr int LPT = SLOTS / NT;             // DMA loads per thread per tensor and block
   static_assert(SLOTS % NT == 0, "block split");
 
+  // two stages each for K and V
   __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KB * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KB * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[KB * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KB * D];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item, XCD-aware: XCD x (= blockIdx % 8) gets a contiguous run of items
-  const int nwg = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int slot = bid >> 3;
-  const int per = nwg >> 3;
-  const int rem = nwg & 7;
-  const int work = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-  const int qt = work % L.Tq;
-  const int bh = work / L.Tq;
+  // ---- work item, XCD-aware.  Workgroups are dispatched round-robin over the 8
+  // XCDs (blockIdx % 8).  Every XCD works on the same (b, h) at a time and takes a
+  // contiguous slice of its query tiles: the head's K/V (tens of MB) then stays in
+  // the shared Infinity Cache while it is in use, and neighbouring query tiles,
+  // whose selections overlap, share each XCD's L2.
+  const int per_xcd = (L.Tq + 7) >> 3;           // query tiles per XCD and head
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int bh = slot / per_xcd;
+  const int qt = xcd * per_xcd + (slot - bh * per_xcd);
+  if (qt >= L.Tq) return;                          // padding workgroup (uniform exit)
   const int h = bh % L.H;
   const int b = bh / L.H;
 
   const int64_t q_first = L.q0 + (int64_t)qt * L.tile;
   const int64_t q_end = L.q0 + L.qlen;
   const int64_t head_off = (int64_t)b * L.sb + (int64_t)h * L.sh;
-  const int32_t* idx_row = idx ? idx + ((int64_t)bh * L.Tq + qt) * L.Ktot : nullptr;
+  const const_i32_t idx_row =
+      (const_i32_t)(idx ? idx + ((int64_t)bh * L.Tq + qt) * L.Ktot : idx);
 
   // ---- Q^T operand: lane holds query (32*wave + l32), d = 16*kk + 8*hi .. +7
   const int64_t my_q = q_first + wave * 32 + l32;
@@ -151,36 +158,43 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     }
   }
 
-  const int bpt = L.tile / KB;
-  const int nsel_blocks = L.Ktot * bpt;
-  int ndense_blocks = 0;
-  for (int r = 0; r < DN.n; ++r) ndense_blocks += (int)((DN.r[r].len + KB - 1) / KB);
-  const int nblk = nsel_blocks + ndense_blocks;
-
-  // ---- DMA mapping: load i of this thread fills 16-byte slot (wave*LPT + i)*64 + lane
-  int dma_row[LPT], dma_col_k[LPT], dma_col_v[LPT];
+  // ---- DMA mapping: load i of this thread fills 16-byte slot (wave*LPT + i)*64 + lane.
+  // Byte offsets from the block's first row are 32-bit and block-independent for
+  // full blocks; the base pointer of a block is wave-uniform.
+  auto dma_row = [&](int i) { return ((wave * LPT + i) * 64 + lane) / CPR; };
+  auto dma_col = [&](int i, bool is_v) {
+    const int r = dma_row(i);
+    const int pc = ((wave * LPT + i) * 64 + lane) % CPR;   // physical chunk
+    return (pc ^ (is_v ? swz_v<CPR>(r) : swz_k<CPR>(r))) * 8;
+  };
+  uint32_t koff[LPT], voff[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int s = (wave * LPT + i) * 64 + lane;
-    dma_row[i] = s / CPR;
-    const int pc = s % CPR;                      // physical chunk
-    dma_col_k[i] = (pc ^ swz_k<CPR>(dma_row[i])) * 8;
-    dma_col_v[i] = (pc ^ swz_v<CPR>(dma_row[i])) * 8;
+    koff[i] = (uint32_t)(((int64_t)dma_row(i) * L.sn + dma_col(i, false)) * 2);
+    voff[i] = (uint32_t)(((int64_t)dma_row(i) * L.sn + dma_col(i, true)) * 2);
   }
-  auto issue = [&](int bi, uint16_t* kd, uint16_t* vd) -> int {
-    const Block blk = key_block(L, DN, idx_row, nsel_blocks, bpt, bi);
-    if (blk.n <= 0) return 0;
-    const uint16_t* kb = k + head_off + blk.start * L.sn;
-    const uint16_t* vb = v + head_off + blk.start * L.sn;
+  const char* kbase = reinterpret_cast<const char*>(k + head_off);
+  const char* vbase = reinterpret_cast<const char*>(v + head_off);
+  auto dma = [&](const char* base, const uint32_t* off, bool is_v, const Block& blk,
+                 uint16_t* dst) {
+    const char* g = base + blk.start * L.sn * 2;
+    if (blk.n == KB) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int64_t r = dma_row[i] < blk.n ? dma_row[i] : blk.n - 1;   // clamp past the end
-      char* lk = reinterpret_cast<char*>(kd) + (wave * LPT + i) * 1024;
-      char* lv = reinterpret_cast<char*>(vd) + (wave * LPT + i) * 1024;
-      __builtin_amdgcn_global_load_lds((void*)(kb + r * L.sn + dma_col_k[i]), (lds_void_t)lk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((void*)(vb + r * L.sn + dma_col_v[i]), (lds_void_t)lv, 16, 0, 0);
+      for (int i = 0; i < LPT; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(g + off[i]),
+                                         (lds_void_t)(reinterpret_cast<char*>(dst) + (wave * LPT + i) * 1024),
+                                         16, 0, 0);
+    } else {
+      // partial block: rows past the end repeat the last row (masked later)
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int r = dma_row(i) < blk.n ? dma_row(i) : blk.n - 1;
+        const uint32_t o = (uint32_t)(((int64_t)r * L.sn + dma_col(i, is_v)) * 2);
+        __builtin_amdgcn_global_load_lds((const void*)(g + o),
+                                         (lds_void_t)(reinterpret_cast<char*>(dst) + (wave * LPT + i) * 1024),
+                                         16, 0, 0);
+      }
     }
-    return blk.n;
   };
 
   f32x16 o[D / 32];
@@ -190,28 +204,35 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float m_run = -INFINITY;
   float l_run = 0.f;
-
-  // per-lane operand addresses that do not depend on the block
-  // K (A of S^T): row mb*32 + l32, logical chunk 2*kk + hi
-  // V^T (A of O^T) via transposing reads: group G = lane/16, j = lane%16
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int vg2 = (lane >> 4) & 1;
   const int vj = lane & 15;
 
-  // One block: wait for its DMA, barrier, start the next block's DMA into the other
-  // stage, then both products.  ST is the stage of this block (a compile-time
-  // constant, so every LDS access names its buffer statically).
-  int cur_n = nblk > 0 ? issue(0, Ks0, Vs0) : 0;
-  auto step = [&](auto stage, int bi) {
+  // ---- pipeline.  Block i's K sits in Ks[i%2], its V in Vs[i%2].  In iteration i:
+  //   S^T = K_i Q^T and the softmax (reads Ks[i%2])
+  //   wait for this wave's DMA, barrier          -> V_i and K_{i+1} visible to all waves
+  //   V_i^T reads (Vs[i%2])
+  //   DMA K_{i+2} -> Ks[i%2], V_{i+1} -> Vs[(i+1)%2]   (both stages were last read
+  //                                                       before this barrier)
+  //   O^T += V_i^T P_i^T
+  // so every DMA has a whole iteration to land and there is one barrier per block.
+  BlockIter it;
+  Block b0 = it.next(L, DN, idx_row);
+  Block b1 = it.next(L, DN, idx_row);
+  if (b0.n > 0) {
+    dma(kbase, koff, false, b0, Ks0);
+    dma(vbase, voff, true, b0, Vs0);
+  }
+  if (b1.n > 0) dma(kbase, koff, false, b1, Ks1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+
+  auto step = [&](auto stage) {
     constexpr int ST = decltype(stage)::value;
     uint16_t* Kc = ST ? Ks1 : Ks0;
     uint16_t* Vc = ST ? Vs1 : Vs0;
-    const int n = cur_n;
-    // this wave's DMA for block bi (the only loads in flight) has landed; the barrier
-    // then makes every wave's part visible and frees the other stage
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
-    if (bi + 1 < nblk) cur_n = ST ? issue(bi + 1, Ks0, Vs0) : issue(bi + 1, Ks1, Vs1);
-    if (n <= 0) return;
+    const int n = b0.n;
+    const Block b2 = it.next(L, DN, idx_row);
 
     // ---- S^T = K Q^T for 64 keys: two 32-key halves
     f32x16 s[2];
@@ -258,15 +279,26 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
-        l_run += pe;
-        pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)pe;
-      }
-
-    // ---- O^T += V^T P^T
+      for (int e = 0; e < 16; ++e)
+        pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
+    // row sum of the bf16 weights the second product uses (two per instruction)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int c = 0; c < 4; ++c) {
+      const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
+      const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, l_run, false);
+    }
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA (V_i, K_{i+1}) landed
+    __syncthreads();
+
+    // ---- V^T operands of this block, then the next DMA, then O^T += V^T P^T
+    bf16x8 va[D / 32][4];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         s16x4 part[2];
@@ -281,14 +313,22 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
         // the two halves as one 16-byte operand (whole-vector cast: building it
         // element by element through bf16 scalars is lowered wrongly by the compiler)
         const s16x8 both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, both);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], o[db], 0, 0, 0);
+        va[db][c] = __builtin_bit_cast(bf16x8, both);
       }
-    }
+    if (b2.n > 0) dma(kbase, koff, false, b2, Kc);
+    if (b1.n > 0) dma(vbase, voff, true, b1, ST ? Vs0 : Vs1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[c], o[db], 0, 0, 0);
+    b0 = b1;
+    b1 = b2;
   };
-  for (int bi = 0; bi < nblk; bi += 2) {
-    step(std::integral_constant<int, 0>{}, bi);
-    if (bi + 1 < nblk) step(std::integral_constant<int, 1>{}, bi + 1);
+  while (b0.n > 0) {
+    step(std::integral_constant<int, 0>{});
+    if (b0.n <= 0) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and store
@@ -322,7 +362,8 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void* q, const void* k,
                               const void* v, const int32_t* idx, float scale, void* out, float* lse,
                               hipStream_t s) {
-  const int64_t nwork = (int64_t)L.B * L.H * L.Tq;
+  const int64_t per_xcd = (L.Tq + 7) / 8;
+  const int64_t nwork = (int64_t)L.B * L.H * per_xcd * 8;
   if (nwork > 0x7FFFFFFF) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
   dim3 grid((unsigned)nwork);

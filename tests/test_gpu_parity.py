@@ -230,9 +230,12 @@ def test_attention_with_oracle_indices(name):
     got = np.concatenate([_gpu_rows(c, o, b, h, i) for (b, h, i) in res])
     ref = np.concatenate([r[0] for r in res.values()])
     check_attn(got, ref)
+    # the kernel normalises by the sum of the bf16-rounded weights that also multiply V
+    # (each within 2^-9 relative of the exact weight), so |lse - lse_ref| <= 2^-9
+    # up to fp32 rounding
     for (b, h, i), (_, l_ref) in res.items():
         r0 = i * c.tile
-        assert np.abs(lse[b, h, r0:r0 + len(l_ref)] - l_ref).max() < 2e-4
+        assert np.abs(lse[b, h, r0:r0 + len(l_ref)] - l_ref).max() <= 2.0 ** -9
     # rows outside the query segment are left untouched (zeros from the caller)
     mask = np.ones(c.n_tokens, bool)
     mask[c.query[0]:c.query[0] + c.query[1]] = False
