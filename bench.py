@@ -267,6 +267,22 @@ def cpu_baseline(lay, log, budget_s=20.0):
     }
 
 
+def recorded_traffic(workload):
+    """HBM-side bytes per attention launch from the committed rocprofv3 byte-counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain 1 GiB copy), or None when no summary
+    exists for this workload or the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_sparse_attn_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    with open(os.path.join(ROOT, t["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["source_sha256"]:
+            return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -296,6 +312,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lay, log)
     achieved = res["actual_tflops_attn"]
+    traffic = recorded_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(res["dense_equiv_tflops_step"], 3),
@@ -322,7 +339,8 @@ def main():
         "speedup_vs_dense": round(res["speedup_vs_dense"], 2) if "speedup_vs_dense" in res else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": (round(traffic / 1e9, 2) if traffic else None),
+                     "traffic_unit": "GB per launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel": "sparse_attn_kernel", "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
         "cpu_baseline": cpu,
         "also": also,
