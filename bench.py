@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time selection + attention on every workload (field 'sweep')")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (byte-counter calibration)")
     return ap.parse_args()
@@ -308,6 +310,21 @@ def main():
                              not args.no_dense, log)
         also = res2
         del lay2
+    sweep = None
+    if args.sweep:
+        sweep = {}
+        for name in ("tiny", "mid", "t2v5s", "r2va", "t2v14s"):
+            if name == args.workload:
+                r = res
+            else:
+                lay_s, r = measure(name, max(3, args.steps // 2), 1, args.kernel_reps, args.dense_reps,
+                                   False, log)
+                del lay_s
+            sweep[name] = {k: round(r[k], 4) for k in ("ms_per_step", "selector_ms", "attn_ms",
+                                                       "actual_tflops_attn", "dense_equiv_tflops_step",
+                                                       "sparsity_actual")}
+            import torch
+            torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lay, log)
@@ -344,6 +361,7 @@ def main():
                      "kernel": "sparse_attn_kernel", "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
         "cpu_baseline": cpu,
         "also": also,
+        "sweep": sweep,
         "detail": res,
     }
     print(json.dumps(line))

@@ -28,7 +28,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLdsScoreBudget = 128 * 1024;   // bytes of LDS for the score block
+constexpr int kHistCopies = 4;                 // radix histograms per wave
 
 // float -> uint32 whose unsigned order is the float order; -0 maps like +0
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -50,6 +50,7 @@ __device__ __forceinline__ int prefix_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+template <int kMaxKSteps>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
                                                               const float* __restrict__ q_hat,
                                                               const float* __restrict__ k_hat,
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
   extern __shared__ uint32_t smem[];
   const int Tk = L.Tk;
   uint32_t* keys = smem;                       // [R][Tk]
-  uint32_t* hist_all = smem + (size_t)R * Tk;  // [kWaves][256]
+  uint32_t* hist_all = smem + (size_t)R * Tk;  // [kWaves][kHistCopies][256]
 
   const int b = blockIdx.z;
   const int h = blockIdx.y;
@@ -72,48 +73,80 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
 
   // ---- 1. scores ------------------------------------------------------------------
   {
-    // A operand (query rows): lane holds row (lane % 16), k = 8*(lane/16) .. +7 per 32-step
+    // A operand (query rows): lane holds row (lane % 16), k = 8*(lane/16) .. +7 of each
+    // 32-wide step; split into hi/lo once.  B operand (key tiles): 16-byte loads of
+    // k_hat, prefetched one column block ahead, split per block.
     const int arow = lane & 15;
     const int kq = (lane >> 4) * 8;
     const int ksteps = (P + 31) / 32;
-    const float* qrow = q_hat + (bh * L.Tq + row0 + arow) * P;
+    const float* __restrict__ qrow = q_hat + (bh * L.Tq + row0 + arow) * P;
     const bool arow_ok = arow < nrows;
-    for (int cb = wave; cb * 16 < Tk; cb += kWaves) {
+    bf16x8 ah[kMaxKSteps], al[kMaxKSteps];
+#pragma unroll
+    for (int ks = 0; ks < kMaxKSteps; ++ks) {
+      float xa[8];
+      const int c0 = ks * 32 + kq;
+      const bool ok = ks < ksteps && arow_ok && c0 < P;
+      const float4 lo4 = ok ? *reinterpret_cast<const float4*>(qrow + c0) : make_float4(0, 0, 0, 0);
+      const float4 hi4 = ok ? *reinterpret_cast<const float4*>(qrow + c0 + 4) : make_float4(0, 0, 0, 0);
+      xa[0] = lo4.x; xa[1] = lo4.y; xa[2] = lo4.z; xa[3] = lo4.w;
+      xa[4] = hi4.x; xa[5] = hi4.y; xa[6] = hi4.z; xa[7] = hi4.w;
+      split8(xa, ah[ks], al[ks]);
+    }
+    auto load_b = [&](int cb, float4 (&buf)[kMaxKSteps][2]) {
       const int kcol = cb * 16 + (lane & 15);
       const bool kcol_ok = kcol < Tk;
-      const float* krow = k_hat + (bh * Tk + kcol) * P;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < ksteps; ++ks) {
-        const int c0 = ks * 32 + kq;
-        float xa[8], xb[8];
-        const bool in_p = c0 < P;   // P is a multiple of 16 and kq a multiple of 8
+      const float* __restrict__ krow = k_hat + (bh * Tk + (kcol_ok ? kcol : 0)) * P;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          xa[t] = (arow_ok && in_p) ? qrow[c0 + t] : 0.f;
-          xb[t] = (kcol_ok && in_p) ? krow[c0 + t] : 0.f;
+      for (int ks = 0; ks < kMaxKSteps; ++ks) {
+        const int c0 = ks * 32 + kq;
+        const bool ok = ks < ksteps && kcol_ok && c0 < P;
+        buf[ks][0] = ok ? *reinterpret_cast<const float4*>(krow + c0) : make_float4(0, 0, 0, 0);
+        buf[ks][1] = ok ? *reinterpret_cast<const float4*>(krow + c0 + 4) : make_float4(0, 0, 0, 0);
+      }
+    };
+    float4 cur[kMaxKSteps][2], nxt[kMaxKSteps][2];
+    int cb = wave;
+    if (cb * 16 < Tk) load_b(cb, cur);
+    for (; cb * 16 < Tk; cb += kWaves) {
+      const int cb_next = cb + kWaves;
+      if (cb_next * 16 < Tk) load_b(cb_next, nxt);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kMaxKSteps; ++ks) {
+        if (ks < ksteps) {
+          float xb[8] = {cur[ks][0].x, cur[ks][0].y, cur[ks][0].z, cur[ks][0].w,
+                         cur[ks][1].x, cur[ks][1].y, cur[ks][1].z, cur[ks][1].w};
+          bf16x8 bh8, bl8;
+          split8(xb, bh8, bl8);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh8, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl8, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh8, acc, 0, 0, 0);
         }
-        bf16x8 ah, al, bh8, bl8;
-        split8(xa, ah, al);
-        split8(xb, bh8, bl8);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh8, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl8, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh8, acc, 0, 0, 0);
       }
       // C layout: lane holds column (lane % 16), rows 4*(lane/16) + j
+      const int kcol = cb * 16 + (lane & 15);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = (lane >> 4) * 4 + j;
-        if (r < nrows && kcol_ok) {
+        if (r < nrows && kcol < Tk) {
           keys[r * Tk + kcol] = order_key(acc[j]);
           if (scores) scores[(bh * L.Tq + row0 + r) * Tk + kcol] = acc[j];
         }
+      }
+#pragma unroll
+      for (int ks = 0; ks < kMaxKSteps; ++ks) {
+        cur[ks][0] = nxt[ks][0];
+        cur[ks][1] = nxt[ks][1];
       }
     }
   }
   __syncthreads();
 
   // ---- 2. top-k per (row, segment), one wave each ------------------------------------
-  uint32_t* hist = hist_all + wave * 256;
+  // each wave keeps kHistCopies histograms (lane % kHistCopies picks one) so lanes
+  // whose keys share a digit rarely hit the same LDS word in one atomic
+  uint32_t* hist = hist_all + wave * (kHistCopies * 256);
   for (int item = wave; item < nrows * L.n_seg; item += kWaves) {
     const int r = item / L.n_seg;
     const int s = item - r * L.n_seg;
@@ -132,19 +165,24 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
     int remaining = K;   // how many still to take from the elements matching `prefix`
     for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) hist[lane * 4 + t] = 0u;
+      for (int t = 0; t < kHistCopies * 4; ++t) hist[t * 64 + lane] = 0u;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       for (int j = lane; j < T; j += 64) {
         const uint32_t key = row[j];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFFu], 1u);
+        if ((key & pmask) == prefix)
+          atomicAdd(&hist[(lane % kHistCopies) * 256 + ((key >> shift) & 0xFFu)], 1u);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
       // lane i owns digits 255-4i .. 252-4i (descending); inclusive scan of counts
       uint32_t c[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) c[t] = hist[255 - (lane * 4 + t)];
+      for (int t = 0; t < 4; ++t) {
+        c[t] = 0u;
+#pragma unroll
+        for (int cp = 0; cp < kHistCopies; ++cp) c[t] += hist[cp * 256 + 255 - (lane * 4 + t)];
+      }
       const uint32_t local = c[0] + c[1] + c[2] + c[3];
       uint32_t incl = local;
 #pragma unroll
@@ -201,7 +239,11 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
 }  // namespace
 
 int score_rows_per_block(int Tk) {
-  int r = kLdsScoreBudget / (Tk * 4);
+  // Prefer a block that lets two workgroups share a CU (<= 78 KB of LDS each); fall
+  // back to one workgroup per CU with up to 144 KB when fewer than 8 rows would fit.
+  const int hist = kWaves * kHistCopies * 256 * 4;
+  int r = (78 * 1024 - hist) / (Tk * 4);
+  if (r < 8) r = (144 * 1024 - hist) / (Tk * 4);
   if (r > 16) r = 16;
   if (r < 1) r = 1;
   return r;
@@ -210,15 +252,26 @@ int score_rows_per_block(int Tk) {
 hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float* k_hat,
                              int32_t* idx, float* scores, hipStream_t s) {
   const int R = score_rows_per_block(L.Tk);
-  const size_t lds = (size_t)R * L.Tk * 4 + kWaves * 256 * 4;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)score_topk_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  const size_t lds = (size_t)R * L.Tk * 4 + kWaves * kHistCopies * 256 * 4;
   dim3 grid((unsigned)((L.Tq + R - 1) / R), (unsigned)L.H, (unsigned)L.B);
-  hipLaunchKernelGGL(score_topk_kernel, grid, dim3(kThreads), lds, s, L, R, q_hat, k_hat, idx,
-                     scores);
+  // the kernel is instantiated for 32-wide predictor steps: p <= 64, 128, 256
+  auto run = [&](auto kern) -> hipError_t {
+    if (lds > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, L, R, q_hat, k_hat, idx, scores);
+    return hipSuccess;
+  };
+  hipError_t e;
+  if (L.p <= 64)
+    e = run(score_topk_kernel<2>);
+  else if (L.p <= 128)
+    e = run(score_topk_kernel<4>);
+  else
+    e = run(score_topk_kernel<8>);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

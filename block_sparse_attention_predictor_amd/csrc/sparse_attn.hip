@@ -232,7 +232,6 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     uint16_t* Kc = ST ? Ks1 : Ks0;
     uint16_t* Vc = ST ? Vs1 : Vs0;
     const int n = b0.n;
-    const Block b2 = it.next(L, DN, idx_row);
 
     // ---- S^T = K Q^T for 64 keys: two 32-key halves
     f32x16 s[2];
@@ -292,6 +291,8 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
       l_run = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, l_run, false);
     }
 
+    // next block two ahead (its scalar index load overlaps the barrier wait)
+    const Block b2 = it.next(L, DN, idx_row);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA (V_i, K_{i+1}) landed
     __syncthreads();
 
