@@ -9,12 +9,12 @@ Attributes of the binding (``select``, ``sparse_attn``, ``dequant_fp8_e4m3``,
 the shared library.
 """
 
-__all__ = ["select", "sparse_attn", "dequant_fp8_e4m3", "project", "Layer", "VedaError",
+__all__ = ["select", "sparse_attn", "layer_attn", "dequant_fp8_e4m3", "project", "Layer", "VedaError",
            "lib_path", "build"]
 
 
 def __getattr__(name):
-    if name in ("select", "sparse_attn", "dequant_fp8_e4m3", "project", "Layer",
+    if name in ("select", "sparse_attn", "dequant_fp8_e4m3", "project", "Layer", "layer_attn",
                 "VedaError", "lib_path", "layer_from_workload", "select_workspace_bytes",
                 "status_string", "abi_version"):
         from . import binding

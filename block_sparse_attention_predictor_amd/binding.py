@@ -86,6 +86,11 @@ def _load():
         "veda_sparse_attn": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                             ctypes.c_float, P, P, P]),
         "veda_dequant_fp8_e4m3": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
+        "veda_sparse_attn_check": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+                                                  ctypes.c_float, P]),
+        "veda_layer_attn": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+                                           ctypes.POINTER(Range), ctypes.c_int32, ctypes.c_float, P, P, P,
+                                           ctypes.c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -98,7 +103,8 @@ def _load():
 def exported_symbols():
     return [n for n in ("veda_abi_version", "veda_status_string", "veda_k_total", "veda_layer_check",
                         "veda_select_workspace_bytes", "veda_pool_project", "veda_score_topk",
-                        "veda_select", "veda_sparse_attn", "veda_dequant_fp8_e4m3")]
+                        "veda_select", "veda_sparse_attn", "veda_dequant_fp8_e4m3",
+                        "veda_sparse_attn_check", "veda_layer_attn")]
 
 
 def abi_version() -> int:
@@ -245,6 +251,33 @@ def sparse_attn(layer: Layer, q, k, v, idx, dense: Sequence[Tuple[int, int]] = (
                                   float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "veda_sparse_attn")
     return (out, lse) if want_lse else out
+
+
+def layer_attn(layer: Layer, q, k, v, wq, wk, dense: Sequence[Tuple[int, int]] = (),
+               dense_queries: Sequence[Tuple[int, int]] = (), scale: float = 0.0, out=None,
+               idx=None, workspace=None, stream=None):
+    """One full layer: selection + sparse attention for the query segment, dense attention
+    for every range in dense_queries.  Returns (out, idx)."""
+    _check_qkv(layer, q, k, v)
+    dev = q.device
+    if out is None:
+        out = torch.zeros_like(q)
+    else:
+        _check_qkv(layer, out)
+    if idx is None:
+        idx = torch.empty((layer.B, layer.H, layer.Tq, layer.Ktot), dtype=torch.int32, device=dev)
+    nbytes = select_workspace_bytes(layer)
+    if nbytes == 0:
+        _check(_load().veda_layer_check(ctypes.byref(layer), 1), "veda_layer_attn")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    darr, nd = dense_ranges(list(dense))
+    qarr, nq = dense_ranges(list(dense_queries))
+    st = _load().veda_layer_attn(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk),
+                                 darr, nd, qarr, nq, float(scale), _ptr(out), _ptr(idx),
+                                 _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "veda_layer_attn")
+    return out, idx
 
 
 def dequant_fp8_e4m3(codes: torch.Tensor, pow2_exp: int = 0, stream=None) -> torch.Tensor:

@@ -181,19 +181,24 @@ int veda_select(const veda_layer* layer, const void* q, const void* k, const voi
   return hip_status(veda::launch_score_topk(D, qh, kh, idx, scores_opt, s));
 }
 
-int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
-                     const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
-                     void* out, float* lse_opt, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check veda_sparse_attn makes before launching; dd receives the dense ranges.
+int sparse_attn_check(const veda_layer* layer, const void* q, const void* k, const void* v,
+                      const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
+                      const void* out, veda::DenseDev* dd) {
   int st = check_layer(layer, false);
   if (st != VEDA_OK) return st;
   if (!q || !k || !v || !out) return VEDA_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VEDA_EINVAL;
-  if (lse_opt && !aligned16(lse_opt)) return VEDA_EINVAL;
   if (n_dense < 0) return VEDA_EINVAL;
   if (n_dense > VEDA_MAX_DENSE) return VEDA_EUNSUPPORTED;
   if (n_dense > 0 && !dense) return VEDA_EINVAL;
   if (!(std::isfinite(scale)) || scale < 0.f) return VEDA_EINVAL;
   int64_t dense_tokens = 0;
+  veda::DenseDev DD{};
   for (int i = 0; i < n_dense; ++i) {
     if (dense[i].len < 0) return VEDA_EINVAL;
     if (!inside(dense[i], layer->n_tokens)) return VEDA_ERANGE;
@@ -202,22 +207,89 @@ int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, cons
     for (int j = 0; j < i; ++j)
       if (overlap(dense[i], dense[j])) return VEDA_ERANGE;
     dense_tokens += dense[i].len;
-  }
-  LayerDev D = to_dev(layer);
-  if (D.Tq == 0) return VEDA_OK;
-  if (D.Ktot == 0 && dense_tokens == 0) return VEDA_ENOKEYS;
-  if (D.Ktot > 0 && !idx) return VEDA_EINVAL;
-  if (idx && !aligned16(idx)) return VEDA_EINVAL;
-  veda::DenseDev DD{};
-  for (int i = 0; i < n_dense; ++i) {
     if (dense[i].len == 0) continue;
     DD.r[DD.n].start = dense[i].start;
     DD.r[DD.n].len = dense[i].len;
     DD.n++;
   }
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) {
+    if (dd) *dd = DD;
+    return VEDA_OK;
+  }
+  if (D.Ktot == 0 && dense_tokens == 0) return VEDA_ENOKEYS;
+  if (!idx && D.Ktot != D.Tk) return VEDA_EINVAL;   // no index: every tile of every segment
+  if (idx && !aligned16(idx)) return VEDA_EINVAL;
+  if (dd) *dd = DD;
+  return VEDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int veda_sparse_attn_check(const veda_layer* layer, const void* q, const void* k, const void* v,
+                           const int32_t* idx, const veda_range* dense, int32_t n_dense,
+                           float scale, const void* out) {
+  return sparse_attn_check(layer, q, k, v, idx, dense, n_dense, scale, out, nullptr);
+}
+
+int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
+                     const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
+                     void* out, float* lse_opt, void* stream) {
+  veda::DenseDev DD{};
+  int st = sparse_attn_check(layer, q, k, v, idx, dense, n_dense, scale, out, &DD);
+  if (st != VEDA_OK) return st;
+  if (lse_opt && !aligned16(lse_opt)) return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) return VEDA_OK;
   if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
   return hip_status(veda::launch_sparse_attn(D, DD, q, k, v, idx, scale, out, lse_opt,
                                              (hipStream_t)stream));
+}
+
+int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
+                    const void* wq, const void* wk, const veda_range* dense, int32_t n_dense,
+                    const veda_range* dense_queries, int32_t n_dense_queries, float scale,
+                    void* out, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_layer(layer, true);
+  if (st != VEDA_OK) return st;
+  if (!v || !out) return VEDA_EINVAL;
+  if (n_dense_queries < 0) return VEDA_EINVAL;
+  if (n_dense_queries > VEDA_MAX_DENSE) return VEDA_EUNSUPPORTED;
+  if (n_dense_queries > 0 && !dense_queries) return VEDA_EINVAL;
+  // every dense query range attends to every key: the same segments with full budgets
+  veda_layer full = *layer;
+  for (int s = 0; s < full.n_seg; ++s) full.budget[s] = (int32_t)((full.seg[s].len + full.tile - 1) / full.tile);
+  for (int i = 0; i < n_dense_queries; ++i) {
+    if (dense_queries[i].len < 0) return VEDA_EINVAL;
+    if (!inside(dense_queries[i], layer->n_tokens)) return VEDA_ERANGE;
+    if (overlap(dense_queries[i], layer->query)) return VEDA_ERANGE;
+    for (int j = 0; j < i; ++j)
+      if (overlap(dense_queries[i], dense_queries[j])) return VEDA_ERANGE;
+  }
+  // argument checks of the three stages, all before the first launch
+  if (!q || !k || !wq || !wk || !idx || !ws) return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  if (ws_bytes < qhat_bytes(D) + khat_bytes(D)) return VEDA_EWORKSPACE;
+  st = veda_sparse_attn_check(layer, q, k, v, idx, dense, n_dense, scale, out);
+  if (st != VEDA_OK) return st;
+  for (int i = 0; i < n_dense_queries; ++i) {
+    full.query = dense_queries[i];
+    st = veda_sparse_attn_check(&full, q, k, v, nullptr, dense, n_dense, scale, out);
+    if (st != VEDA_OK) return st;
+  }
+  st = veda_select(layer, q, k, wq, wk, idx, nullptr, ws, ws_bytes, stream);
+  if (st != VEDA_OK) return st;
+  st = veda_sparse_attn(layer, q, k, v, idx, dense, n_dense, scale, out, nullptr, stream);
+  if (st != VEDA_OK) return st;
+  for (int i = 0; i < n_dense_queries; ++i) {
+    if (dense_queries[i].len == 0) continue;
+    full.query = dense_queries[i];
+    st = veda_sparse_attn(&full, q, k, v, nullptr, dense, n_dense, scale, out, nullptr, stream);
+    if (st != VEDA_OK) return st;
+  }
+  return VEDA_OK;
 }
 
 int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,

@@ -60,7 +60,9 @@ struct Block {
 
 // Walks the key blocks of one (b, h, query tile): the selected tiles of every
 // segment in index order (tiles longer than a block give several blocks; the
-// empty tail of a short last tile gives none), then every dense range.
+// empty tail of a short last tile gives none; index entries of -1 are padding and
+// give none), then every dense range.  Without an index row every tile of every
+// segment is taken, in order.
 struct BlockIter {
   int sel = 0, sub = 0, seg = 0, dr = 0;
   int64_t doff = 0;
@@ -70,7 +72,12 @@ struct BlockIter {
     for (;;) {
       if (sel < L.Ktot) {
         while (sel >= L.seg[seg].koff + L.seg[seg].K) ++seg;
-        const int t = idx_row[sel];
+        const int t = idx_row ? idx_row[sel] : sel - L.seg[seg].koff;
+        if (t < 0) {
+          ++sel;
+          sub = 0;
+          continue;
+        }
         const int64_t rel = (int64_t)t * L.tile + (int64_t)sub * KB;
         const int64_t rem = L.seg[seg].len - rel;
         const int64_t st = L.seg[seg].start + rel;
@@ -332,9 +339,10 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     step(std::integral_constant<int, 1>{});
   }
 
-  // ---- normalise and store
+  // ---- normalise and store (a row with no key at all, possible only when every index
+  // entry is padding and there is no dense range, is written as zeros)
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (q_ok) {
     uint16_t* op = out + head_off + my_q * L.sn;
 #pragma unroll

@@ -147,8 +147,13 @@ int veda_select(const veda_layer* layer, const void* q, const void* k,
  * computed with bf16 matrix cores, fp32 online softmax and fp32 accumulation,
  * rounded to bf16 (nearest even).  Only the query segment's rows of `out` are
  * written.
- *   idx        : int32 [B, H, Tq, Ktot] contiguous.  Entries are NOT re-validated:
- *                an id outside [0, T_s) is undefined behaviour.
+ *   idx        : int32 [B, H, Tq, Ktot] contiguous.  An entry of -1 is padding and
+ *                selects nothing (index producers with fewer tiles for some query
+ *                tiles pad their rows with -1).  Other entries are NOT re-validated:
+ *                an id outside [0, T_s) is undefined behaviour.  A query tile left with
+ *                no key at all (all padding, no dense range) gets zero output rows.
+ *                idx may be NULL when every budget[s] >= T_s: every tile of every
+ *                segment is then attended (dense attention over the segments).
  *   dense      : host array of n_dense ranges (0 <= n_dense <= VEDA_MAX_DENSE),
  *                disjoint from the key segments and from each other.
  *   scale      : softmax scale; 0 selects 1/sqrt(d).
@@ -159,6 +164,35 @@ int veda_select(const veda_layer* layer, const void* q, const void* k,
 int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
                      const int32_t* idx, const veda_range* dense, int32_t n_dense,
                      float scale, void* out, float* lse_opt, void* stream);
+
+/*
+ * Host-only check of a veda_sparse_attn call: returns the status veda_sparse_attn
+ * would return for these arguments without launching anything (lse_opt and stream
+ * are not needed).  No device call.
+ */
+int veda_sparse_attn_check(const veda_layer* layer, const void* q, const void* k, const void* v,
+                           const int32_t* idx, const veda_range* dense, int32_t n_dense,
+                           float scale, const void* out);
+
+/*
+ * One full attention layer as the video model runs it (Veda R2VA record, first
+ * paragraph: the video queries use the selected reference and video tiles; text,
+ * VLM conditioning and audio attention stay dense):
+ *   1. veda_select for the query segment (the generated video)  -> idx;
+ *   2. veda_sparse_attn for the query segment's rows;
+ *   3. for each of the n_dense_queries ranges (text, VLM, audio or reference query
+ *      rows), dense attention over every token of every key segment and every
+ *      dense key range, written at those rows of `out`.
+ * All checks of the three stages are done before the first launch.
+ *   dense_queries : host array (<= VEDA_MAX_DENSE) of query ranges, disjoint from
+ *                   layer->query and from each other (they may overlap key ranges).
+ *   idx, ws, ws_bytes : as for veda_select (idx receives the selection).
+ * Other arguments as for veda_select / veda_sparse_attn.
+ */
+int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
+                    const void* wq, const void* wk, const veda_range* dense, int32_t n_dense,
+                    const veda_range* dense_queries, int32_t n_dense_queries, float scale,
+                    void* out, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * FP8 predictor weights to bf16 at load (step a0; Veda R2VA record: the

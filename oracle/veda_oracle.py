@@ -209,8 +209,8 @@ def select(q_bits, k_bits, wq, wk, tile: int, query: Tuple[int, int],
 
 def attended_tokens(idx_row: np.ndarray, tile: int, segments: Sequence[Tuple[int, int, int]],
                     dense: Sequence[Tuple[int, int]]) -> np.ndarray:
-    """Token positions one query tile attends to: selected tiles of each segment,
-    then every dense range."""
+    """Token positions one query tile attends to: selected tiles of each segment
+    (an entry of -1 is padding and selects nothing), then every dense range."""
     toks = []
     kc = 0
     for (st, ln, bud) in segments:
@@ -218,6 +218,8 @@ def attended_tokens(idx_row: np.ndarray, tile: int, segments: Sequence[Tuple[int
         K = min(bud, T)
         for j in idx_row[kc:kc + K]:
             j = int(j)
+            if j == -1:          # padding entry: selects nothing
+                continue
             if not (0 <= j < T):
                 raise ValueError("tile index out of range")
             toks.append(np.arange(st + j * tile, st + min((j + 1) * tile, ln)))
@@ -254,6 +256,22 @@ def attend_tile(q_bits, k_bits, v_bits, b: int, h: int, qtile: int, idx_row: np.
     if toks.size == 0:
         raise ValueError("query tile attends to no keys")
     qr = bf16_bits_to_f64(q_bits[b, q0:q1, h, :])
+    kr = bf16_bits_to_f64(k_bits[b, toks, h, :])
+    vr = bf16_bits_to_f64(v_bits[b, toks, h, :])
+    return attend_rows(qr, kr, vr, scale)
+
+
+def attend_all_keys(q_bits, k_bits, v_bits, b: int, h: int, rows: Tuple[int, int], segments,
+                    dense, scale: Optional[float] = None):
+    """Dense attention of the query rows [start, start + len) over every token of every
+    key segment and every dense range (the text / VLM / audio / reference query rows
+    of a layer, whose attention stays dense).  Returns (out [len, d], lse [len])."""
+    d = q_bits.shape[3]
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    toks = np.concatenate([np.arange(st, st + ln) for (st, ln, _) in segments] +
+                          [np.arange(st, st + ln) for (st, ln) in dense])
+    qr = bf16_bits_to_f64(q_bits[b, rows[0]:rows[0] + rows[1], h, :])
     kr = bf16_bits_to_f64(k_bits[b, toks, h, :])
     vr = bf16_bits_to_f64(v_bits[b, toks, h, :])
     return attend_rows(qr, kr, vr, scale)

@@ -146,3 +146,32 @@ def test_empty_query_segment_is_a_no_op():
     arr, n = Bnd.dense_ranges([])
     assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, 0, 0.0, fake, None, None) == 0
     assert lib.veda_score_topk(ctypes.byref(L), fake, fake, fake, None, None) == 0
+
+
+def test_layer_attn_and_attention_checks_before_device_calls():
+    lib = Bnd._load()
+    L = _layer()
+    fake = ctypes.c_void_p(0x10000)
+    need = Bnd.select_workspace_bytes(L)
+    dense, nd = Bnd.dense_ranges([(133056, 512), (133568, 256), (133824, 1024)])
+    # a dense query range overlapping the sparse query segment
+    dq, nq = Bnd.dense_ranges([(128000, 2000)])
+    assert lib.veda_layer_attn(ctypes.byref(L), fake, fake, fake, fake, fake, dense, nd, dq, nq, 0.0,
+                               fake, fake, fake, need, None) == -4
+    # dense query ranges overlapping each other
+    dq, nq = Bnd.dense_ranges([(133056, 512), (133100, 10)])
+    assert lib.veda_layer_attn(ctypes.byref(L), fake, fake, fake, fake, fake, dense, nd, dq, nq, 0.0,
+                               fake, fake, fake, need, None) == -4
+    # too small a workspace, missing V
+    dq, nq = Bnd.dense_ranges([(129024, 4032)])
+    assert lib.veda_layer_attn(ctypes.byref(L), fake, fake, fake, fake, fake, dense, nd, dq, nq, 0.0,
+                               fake, fake, fake, need - 1, None) == -3
+    assert lib.veda_layer_attn(ctypes.byref(L), fake, fake, None, fake, fake, dense, nd, dq, nq, 0.0,
+                               fake, fake, fake, need, None) == -1
+    # attention without an index needs every budget to cover its segment
+    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, None, dense, nd, 0.0, fake) == -1
+    Lf = _layer()
+    Lf.budget[0] = 32
+    Lf.budget[1] = 1008
+    assert lib.veda_sparse_attn_check(ctypes.byref(Lf), fake, fake, fake, None, dense, nd, 0.0, fake) == 0
+    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, fake, dense, nd, 0.0, fake) == 0

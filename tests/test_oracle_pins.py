@@ -446,3 +446,40 @@ def test_planted_mistakes_are_caught(monkeypatch):
         with monkeypatch.context() as m:
             m.setattr(O, name, bad)
             assert any(_pins_fail(p) for p in pins), f"planted mistake in {name} not caught"
+
+
+def test_padding_entries_select_nothing():
+    """-1 entries are padding: the same result as leaving the entry out (brute-force mask)."""
+    q, k, v, tile, query, segments, dense = _small_attn_layer(19)
+    B, N, H, d = q.shape
+    idx = np.zeros((1, H, 4, 3), dtype=np.int32)
+    idx[..., 0] = 1
+    idx[..., 1] = 0
+    idx[..., 2] = -1                                  # video segment: one tile + padding
+    res = O.attend(q, k, v, idx, tile, query, segments, dense)
+    qf, kf, vf = (O.bf16_bits_to_f64(x) for x in (q, k, v))
+    for (b, h, i), (out, _) in res.items():
+        q0, q1 = i * tile, min((i + 1) * tile, query[1])
+        mask = np.zeros(N, bool)
+        mask[14 + 4:14 + 7] = True                    # ref segment tile 1 (tokens 18..20)
+        mask[0:4] = True                              # video tile 0
+        for (st, ln) in dense:
+            mask[st:st + ln] = True
+        ref = _sdpa_masked(qf[b, q0:q1, h], kf[b, :, h], vf[b, :, h],
+                           np.broadcast_to(mask, (q1 - q0, N)).copy(), 1 / math.sqrt(d))
+        assert np.allclose(out, ref, rtol=0, atol=1e-13)
+
+
+def test_dense_query_rows_match_sdpa():
+    q, k, v, tile, query, segments, dense = _small_attn_layer(23)
+    qf, kf, vf = (O.bf16_bits_to_f64(x) for x in (q, k, v))
+    keys = np.r_[0:28]
+    keys = keys[(keys < 24) | (keys >= 26)]          # every segment and dense token
+    rows = (21, 3)                                    # e.g. the text tokens as queries
+    for h in range(2):
+        out, lse = O.attend_all_keys(q, k, v, 0, h, rows, segments, dense)
+        qt = torch.from_numpy(qf[0, 21:24, h])[None, None]
+        kt = torch.from_numpy(kf[0, keys, h])[None, None]
+        vt = torch.from_numpy(vf[0, keys, h])[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0].numpy()
+        assert np.allclose(out, ref, rtol=0, atol=1e-13)
