@@ -43,24 +43,26 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="also time selection + attention on every workload (field 'sweep')")
+    ap.add_argument("--no-patterns", action="store_true",
+                    help="skip the budget 16/32/64 and VDN window timings (field 'patterns')")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (byte-counter calibration)")
     return ap.parse_args()
 
 
-def attended_tokens_per_tile(wl, idx: np.ndarray) -> np.ndarray:
-    """Real key tokens each (b, h, query tile) attends to, from the index sets used."""
-    lens = []
-    for s in wl.segments:
+def attended_tokens_per_tile(wl, idx: np.ndarray, widths=None) -> np.ndarray:
+    """Real key tokens each (b, h, query tile) attends to, from the index sets used
+    (a -1 entry ends its segment's block).  widths: index columns per segment."""
+    total = np.zeros(idx.shape[:-1], dtype=np.int64)
+    col = 0
+    for si, s in enumerate(wl.segments):
         T = wl.seg_tiles(s)
         tl = np.full(T, wl.tile, dtype=np.int64)
         tl[-1] = s.length - (T - 1) * wl.tile
-        lens.append(tl)
-    total = np.zeros(idx.shape[:-1], dtype=np.int64)
-    col = 0
-    for s, tl in zip(wl.segments, lens):
-        K = min(s.budget, wl.seg_tiles(s))
-        total += tl[idx[..., col:col + K]].sum(-1)
+        K = widths[si] if widths is not None else min(s.budget, T)
+        blk = idx[..., col:col + K]
+        live = np.cumprod(blk >= 0, axis=-1).astype(bool)
+        total += np.where(live, tl[np.where(live, blk, 0)], 0).sum(-1)
         col += K
     return total + sum(r.length for r in wl.dense)
 
@@ -113,17 +115,32 @@ class Layer:
         self.select()
         self.attn()
 
+    def dense_queries(self):
+        """Every non-video query row (reference image, text, VLM, audio) attends densely."""
+        wl = self.wl
+        return ([(s.start, s.length) for s in wl.segments if s.name != "video"] +
+                [(r.start, r.length) for r in wl.dense])
+
+    def full_layer(self):
+        self.B.layer_attn(self.L, self.qd, self.kd, self.vd, self.wq, self.wk, self.dense,
+                          self.dense_queries(), out=self.out, idx=self.idx, workspace=self.ws)
+
+    def dense_query_flops(self):
+        wl = self.wl
+        nk_all = sum(s.length for s in wl.segments) + sum(r.length for r in wl.dense)
+        return 4.0 * wl.B * wl.H * sum(n for _, n in self.dense_queries()) * nk_all * wl.d
+
     def dense_flops(self):
         wl = self.wl
         nk_all = sum(s.length for s in wl.segments) + sum(r.length for r in wl.dense)
         return 4.0 * wl.B * wl.H * wl.query.length * nk_all * wl.d
 
-    def actual_flops(self, idx_np):
-        per_tile = attended_tokens_per_tile(self.wl, idx_np)          # [B, H, Tq]
+    def actual_flops(self, idx_np, widths=None):
+        per_tile = attended_tokens_per_tile(self.wl, idx_np, widths)  # [B, H, Tq]
         rows = query_rows_per_tile(self.wl)
         return 4.0 * self.wl.d * float((per_tile * rows[None, None, :]).sum())
 
-    def full_layer(self):
+    def full_budget_layer(self):
         full = self.I.with_full_budget(self.wl)
         return self.B.layer_from_workload(full), full
 
@@ -196,11 +213,18 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
         "actual_attn_tflop": flops_actual / 1e12, "dense_equiv_tflop": flops_dense / 1e12,
         "sparsity_actual": 1.0 - flops_actual / flops_dense,
     }
+    # one full layer as the model runs it: also the dense (non-video) query rows
+    lay.full_layer()
+    torch.cuda.synchronize()
+    fl_mean, fl_min, _ = time_events(lay.full_layer, max(3, kernel_reps // 2))
+    res["full_layer_ms"] = fl_mean
+    res["dense_query_rows"] = sum(n for _, n in lay.dense_queries())
+    res["dense_query_tflop"] = lay.dense_query_flops() / 1e12
     # pooling bandwidth: Q rows of the query segment + K rows of every key segment, once
     pool_bytes = 2.0 * wl.B * wl.H * wl.d * (wl.query.length + sum(sg.length for sg in wl.segments))
     res["pool_bytes"] = pool_bytes
     if with_dense:
-        Lf, wlf = lay.full_layer()
+        Lf, wlf = lay.full_budget_layer()
         idx_full = torch.from_numpy(lay.I.full_indices(wl)).to(lay.qd.device)
         lay.attn(idx_full, Lf)
         torch.cuda.synchronize()
@@ -211,6 +235,58 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
         res["speedup_vs_dense"] = d_mean / ms_step
         del idx_full
     return lay, res
+
+
+def measure_patterns(lay, kernel_reps, log):
+    """Other index producers through the same attention kernel: the learned selector at
+    top-k budgets 16 / 32 / 64 per key segment, and the fixed VDN window pattern
+    (chunks of five latent frames, one neighbour chunk each side, boundary anchors)."""
+    import torch
+    wl, B, I = lay.wl, lay.B, lay.I
+    dev = lay.qd.device
+    flops_dense = lay.dense_flops()
+    out = {}
+    for k in (16, 32, 64):
+        wk = I.with_budget(wl, k)
+        Lk = B.layer_from_workload(wk)
+        idx = torch.empty((wl.B, wl.H, wl.n_query_tiles, wk.k_total), dtype=torch.int32, device=dev)
+        ws = torch.empty(B.select_workspace_bytes(Lk) + 256, dtype=torch.uint8, device=dev)
+
+        def sel(Lk=Lk, idx=idx, ws=ws):
+            B.select(Lk, lay.qd, lay.kd, lay.wq, lay.wk, workspace=ws, idx=idx)
+
+        sel()
+        torch.cuda.synchronize()
+        log(f"[{wl.name}] budget {k}")
+        s_ms, _, _ = time_events(sel, kernel_reps)
+        a_ms, _, _ = time_events(lambda: lay.attn(idx, Lk), kernel_reps)
+        fl = lay.actual_flops(idx.cpu().numpy(), [min(k, wl.seg_tiles(sg)) for sg in wl.segments])
+        out[f"budget_{k}"] = {"selector_ms": round(s_ms, 4), "attn_ms": round(a_ms, 4),
+                              "density": round(fl / flops_dense, 4),
+                              "actual_tflops_attn": round(fl / (a_ms * 1e-3) / 1e12, 1)}
+        del idx, ws
+    video = [s for s in wl.segments if s.name == "video"]
+    if len(wl.segments) == 1 and video and video[0].start == wl.query.start \
+            and video[0].length == wl.query.length:
+        ft = wl.grid[1] * wl.grid[2]
+
+        def win():
+            return B.window_indices(lay.L, ft, 5, 1, True)
+
+        idx, Lw = win()
+        torch.cuda.synchronize()
+        log(f"[{wl.name}] VDN window pattern, width {Lw.budget[0]}")
+        p_ms, _, _ = time_events(win, kernel_reps)
+        reps = max(2, kernel_reps // 4)
+        a_ms, _, _ = time_events(lambda: lay.attn(idx, Lw), reps)
+        fl = lay.actual_flops(idx.cpu().numpy(), [int(Lw.budget[0])])
+        out["vdn_window"] = {"chunk_frames": 5, "halo_chunks": 1, "anchors": True,
+                             "width": int(Lw.budget[0]), "indices_ms": round(p_ms, 4),
+                             "attn_ms": round(a_ms, 4), "density": round(fl / flops_dense, 4),
+                             "actual_tflops_attn": round(fl / (a_ms * 1e-3) / 1e12, 1)}
+        del idx
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(lay, log, budget_s=20.0):
@@ -304,6 +380,7 @@ def main():
     lay, res = measure(args.workload, args.steps, args.warmup, args.kernel_reps, args.dense_reps,
                        not args.no_dense, log)
     wl = lay.wl
+    patterns = None if args.no_patterns else measure_patterns(lay, args.kernel_reps, log)
     also = None
     if args.also and args.also != "none" and args.also != args.workload:
         lay2, res2 = measure(args.also, args.steps, args.warmup, args.kernel_reps, args.dense_reps,
@@ -348,6 +425,7 @@ def main():
                    "budgets": {s.name: s.budget for s in wl.segments},
                    "dense_tokens": sum(r.length for r in wl.dense)},
         "selector_ms": round(res["selector_ms"], 4),
+        "full_layer_ms": round(res["full_layer_ms"], 4),
         "attn_ms": round(res["attn_ms"], 4),
         "dense_equiv_tflops_attn": round(res["dense_equiv_tflops_attn"], 2),
         "actual_tflops_attn": round(achieved, 2),
@@ -360,6 +438,7 @@ def main():
                      "traffic_unit": "GB per launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel": "sparse_attn_kernel", "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
         "cpu_baseline": cpu,
+        "patterns": patterns,
         "also": also,
         "sweep": sweep,
         "detail": res,

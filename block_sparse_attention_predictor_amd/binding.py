@@ -91,6 +91,10 @@ def _load():
         "veda_layer_attn": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                            ctypes.POINTER(Range), ctypes.c_int32, ctypes.c_float, P, P, P,
                                            ctypes.c_size_t, P]),
+        "veda_window_width": (ctypes.c_int64, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32]),
+        "veda_window_indices": (ctypes.c_int, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, P, ctypes.c_int32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -104,7 +108,8 @@ def exported_symbols():
     return [n for n in ("veda_abi_version", "veda_status_string", "veda_k_total", "veda_layer_check",
                         "veda_select_workspace_bytes", "veda_pool_project", "veda_score_topk",
                         "veda_select", "veda_sparse_attn", "veda_dequant_fp8_e4m3",
-                        "veda_sparse_attn_check", "veda_layer_attn")]
+                        "veda_sparse_attn_check", "veda_layer_attn", "veda_window_width",
+                        "veda_window_indices")]
 
 
 def abi_version() -> int:
@@ -278,6 +283,33 @@ def layer_attn(layer: Layer, q, k, v, wq, wk, dense: Sequence[Tuple[int, int]] =
                                  _ptr(workspace), nbytes, _stream(stream))
     _check(st, "veda_layer_attn")
     return out, idx
+
+
+def window_width(layer: Layer, frame_tokens: int, chunk_frames: int = 5, halo_chunks: int = 1,
+                 anchors: bool = True) -> int:
+    """Longest row (key tiles) of the sliding frame-chunk window pattern."""
+    w = _load().veda_window_width(ctypes.byref(layer), int(frame_tokens), int(chunk_frames),
+                                  int(halo_chunks), 1 if anchors else 0)
+    if w < 0:
+        raise VedaError(int(w), "veda_window_width")
+    return int(w)
+
+
+def window_indices(layer: Layer, frame_tokens: int, chunk_frames: int = 5, halo_chunks: int = 1,
+                   anchors: bool = True, width: Optional[int] = None, device=None, stream=None):
+    """Window-pattern tile indices int32 [B, H, Tq, width], rows ascending, -1 padded.
+    Returns (idx, attention_layer): the copy of `layer` whose budget[0] is width."""
+    if width is None:
+        width = window_width(layer, frame_tokens, chunk_frames, halo_chunks, anchors)
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    idx = torch.empty((layer.B, layer.H, layer.Tq, width), dtype=torch.int32, device=dev)
+    st = _load().veda_window_indices(ctypes.byref(layer), int(frame_tokens), int(chunk_frames),
+                                     int(halo_chunks), 1 if anchors else 0, _ptr(idx), int(width),
+                                     _stream(stream))
+    _check(st, "veda_window_indices")
+    att = Layer.from_buffer_copy(layer)
+    att.budget[0] = width
+    return idx, att
 
 
 def dequant_fp8_e4m3(codes: torch.Tensor, pow2_exp: int = 0, stream=None) -> torch.Tensor:

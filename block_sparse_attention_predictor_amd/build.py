@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libveda.so")
-SOURCES = ["api.cpp", "dequant.hip", "pool_project.hip", "score_topk.hip", "sparse_attn.hip"]
+SOURCES = ["api.cpp", "dequant.hip", "pool_project.hip", "score_topk.hip", "sparse_attn.hip",
+           "patterns.hip"]
 ARCH = "gfx950"
 
 

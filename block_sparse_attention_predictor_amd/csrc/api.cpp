@@ -292,6 +292,55 @@ int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const
   return VEDA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+int window_check(const veda_layer* layer, int64_t frame_tokens, int32_t chunk_frames,
+                 int32_t halo_chunks, int32_t anchors, veda::WindowPattern* P) {
+  int st = check_layer(layer, false);
+  if (st != VEDA_OK) return st;
+  if (layer->n_seg != 1) return VEDA_EUNSUPPORTED;
+  if (layer->seg[0].start != layer->query.start || layer->seg[0].len != layer->query.len)
+    return VEDA_ERANGE;
+  if (frame_tokens < 1 || chunk_frames < 1 || halo_chunks < 0 || (anchors != 0 && anchors != 1))
+    return VEDA_EINVAL;
+  P->frame_tokens = frame_tokens;
+  P->chunk_frames = chunk_frames;
+  P->halo_chunks = halo_chunks;
+  P->anchors = anchors;
+  return VEDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t veda_window_width(const veda_layer* layer, int64_t frame_tokens, int32_t chunk_frames,
+                          int32_t halo_chunks, int32_t anchors) {
+  veda::WindowPattern P{};
+  const int st = window_check(layer, frame_tokens, chunk_frames, halo_chunks, anchors, &P);
+  if (st != VEDA_OK) return st;
+  return veda::window_max_tiles(layer->query.start, layer->query.len, layer->tile, layer->seg[0].len, P);
+}
+
+int veda_window_indices(const veda_layer* layer, int64_t frame_tokens, int32_t chunk_frames,
+                        int32_t halo_chunks, int32_t anchors, int32_t* idx, int32_t width,
+                        void* stream) {
+  veda::WindowPattern P{};
+  int st = window_check(layer, frame_tokens, chunk_frames, halo_chunks, anchors, &P);
+  if (st != VEDA_OK) return st;
+  if (!idx || !aligned16(idx)) return VEDA_EINVAL;
+  const int64_t need = veda::window_max_tiles(layer->query.start, layer->query.len, layer->tile,
+                                              layer->seg[0].len, P);
+  if (width < need || width > ceil_div(layer->seg[0].len, layer->tile)) return VEDA_EINVAL;
+  const int64_t Tq = ceil_div(layer->query.len, layer->tile);
+  if (Tq == 0) return VEDA_OK;
+  return hip_status(veda::launch_window_indices(layer->query.start, layer->query.len, layer->tile,
+                                                layer->seg[0].len, (int32_t)Tq, layer->B * layer->H, P,
+                                                idx, width, (hipStream_t)stream));
+}
+
 int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,
                           void* stream) {
   if (n < 0) return VEDA_EINVAL;

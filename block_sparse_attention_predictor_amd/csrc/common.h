@@ -52,6 +52,18 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& D, const void* 
 hipError_t launch_dequant_e4m3(const uint8_t* src, void* dst, int64_t n, int32_t pow2_exp,
                                hipStream_t s);
 
+// Sliding frame-chunk window pattern (see patterns.hip).
+struct WindowPattern {
+  int64_t frame_tokens;   // tokens per latent frame
+  int32_t chunk_frames;   // frames per chunk
+  int32_t halo_chunks;    // neighbouring chunks on each side
+  int32_t anchors;        // 1: first and last frame are global
+};
+int64_t window_max_tiles(int64_t q0, int64_t qlen, int64_t tile, int64_t seg_len, const WindowPattern& P);
+hipError_t launch_window_indices(int64_t q0, int64_t qlen, int64_t tile, int64_t seg_len, int32_t Tq,
+                                 int32_t BH, const WindowPattern& P, int32_t* idx, int32_t kmax,
+                                 hipStream_t s);
+
 // Rows of the score block one selection workgroup handles for Tk key tiles.
 int score_rows_per_block(int Tk);
 

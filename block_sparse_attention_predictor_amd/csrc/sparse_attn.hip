@@ -60,8 +60,9 @@ struct Block {
 
 // Walks the key blocks of one (b, h, query tile): the selected tiles of every
 // segment in index order (tiles longer than a block give several blocks; the
-// empty tail of a short last tile gives none; index entries of -1 are padding and
-// give none), then every dense range.  Without an index row every tile of every
+// empty tail of a short last tile gives none; an index entry of -1 ends its
+// segment's block: it and the later entries of that block give none), then every
+// dense range.  Without an index row every tile of every
 // segment is taken, in order.
 struct BlockIter {
   int sel = 0, sub = 0, seg = 0, dr = 0;
@@ -73,8 +74,8 @@ struct BlockIter {
       if (sel < L.Ktot) {
         while (sel >= L.seg[seg].koff + L.seg[seg].K) ++seg;
         const int t = idx_row ? idx_row[sel] : sel - L.seg[seg].koff;
-        if (t < 0) {
-          ++sel;
+        if (t < 0) {   // padding: the rest of this segment's block is unused
+          sel = L.seg[seg].koff + L.seg[seg].K;
           sub = 0;
           continue;
         }

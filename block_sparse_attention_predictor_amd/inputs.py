@@ -353,3 +353,9 @@ def full_indices(wl: Workload) -> np.ndarray:
 def with_full_budget(wl: Workload) -> Workload:
     segs = tuple(Segment(s.name, s.start, s.length, wl.seg_tiles(s)) for s in wl.segments)
     return Workload(**{**wl.__dict__, "segments": segs})
+
+
+def with_budget(wl: Workload, budget: int) -> Workload:
+    """The same layer with one top-k budget for every key segment (budget sweeps)."""
+    segs = tuple(Segment(s.name, s.start, s.length, budget) for s in wl.segments)
+    return Workload(**{**wl.__dict__, "segments": segs})

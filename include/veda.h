@@ -147,9 +147,11 @@ int veda_select(const veda_layer* layer, const void* q, const void* k,
  * computed with bf16 matrix cores, fp32 online softmax and fp32 accumulation,
  * rounded to bf16 (nearest even).  Only the query segment's rows of `out` are
  * written.
- *   idx        : int32 [B, H, Tq, Ktot] contiguous.  An entry of -1 is padding and
- *                selects nothing (index producers with fewer tiles for some query
- *                tiles pad their rows with -1).  Other entries are NOT re-validated:
+ *   idx        : int32 [B, H, Tq, Ktot] contiguous.  An entry of -1 is padding: it
+ *                and every later entry of the same segment's block select nothing
+ *                (producers with fewer tiles for some query tiles end those rows'
+ *                segment blocks with -1; the kernel skips the rest of the block at
+ *                once).  Other entries are NOT re-validated:
  *                an id outside [0, T_s) is undefined behaviour.  A query tile left with
  *                no key at all (all padding, no dense range) gets zero output rows.
  *                idx may be NULL when every budget[s] >= T_s: every tile of every
@@ -193,6 +195,32 @@ int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const
                     const void* wq, const void* wk, const veda_range* dense, int32_t n_dense,
                     const veda_range* dense_queries, int32_t n_dense_queries, float scale,
                     void* out, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fixed-pattern index producer: sliding windows of frame chunks with boundary
+ * anchors (the VDN analysis, "The mechanism: solving instead of stepping": chunks
+ * of consecutive latent frames attend to themselves and their neighbouring chunks;
+ * every frame also attends to the first and last frames, which attend to
+ * everything).  Produced at tile granularity for veda_sparse_attn: query tile i
+ * takes every key tile that overlaps a key frame of any of its query frames.
+ *   layer        : one key segment equal to the query segment (the video); frames
+ *                  count from its start, frame_tokens tokens each.
+ *   chunk_frames : frames per chunk (>= 1); halo_chunks: neighbours on each side (>= 0);
+ *   anchors      : 1 to add the first/last-frame anchors, 0 for windows only.
+ * veda_window_width returns the longest row in tiles, or a negative status
+ * (VEDA_EUNSUPPORTED unless n_seg == 1, VEDA_ERANGE unless seg[0] equals the query
+ * segment, VEDA_EINVAL for a bad pattern).  veda_window_indices writes
+ * idx int32 [B, H, Tq, width] (device, 16-byte aligned, caller-owned): each row
+ * ascending, then -1 padding; every (b, h) gets the same rows.  It needs
+ * longest row <= width <= ceil(seg[0].len / tile) (else VEDA_EINVAL) and is
+ * asynchronous on `stream`.  Feed idx to veda_sparse_attn on the same layer with
+ * budget[0] = width.
+ */
+int64_t veda_window_width(const veda_layer* layer, int64_t frame_tokens, int32_t chunk_frames,
+                          int32_t halo_chunks, int32_t anchors);
+int veda_window_indices(const veda_layer* layer, int64_t frame_tokens, int32_t chunk_frames,
+                        int32_t halo_chunks, int32_t anchors, int32_t* idx, int32_t width,
+                        void* stream);
 
 /*
  * FP8 predictor weights to bf16 at load (step a0; Veda R2VA record: the

@@ -25,6 +25,15 @@ layer of a video diffusion transformer):
       key range (text / VLM / audio stay dense, same record), with a two-pass
       softmax at scale 1/sqrt(d)
 
+and, as a fixed index producer beside the learned one:
+
+  P1  the sliding frame-chunk window with boundary anchors   (VDN article, "The
+      mechanism: solving instead of stepping": chunks of consecutive latent frames
+      attend to themselves and their neighbouring chunks; every frame also attends
+      to the first and last frames, which attend to every frame), carried to tile
+      granularity: a query tile takes a key tile when some query token of it may
+      attend some key token of the other
+
 All arithmetic is float64 from the exact bf16 (or E4M3) input values.  Library
 primitives used as single steps: numpy mean over a slice, matmul, stable argsort,
 exp and log.  There is no blocking, fusion or reordering beyond the definitions.
@@ -209,8 +218,10 @@ def select(q_bits, k_bits, wq, wk, tile: int, query: Tuple[int, int],
 
 def attended_tokens(idx_row: np.ndarray, tile: int, segments: Sequence[Tuple[int, int, int]],
                     dense: Sequence[Tuple[int, int]]) -> np.ndarray:
-    """Token positions one query tile attends to: selected tiles of each segment
-    (an entry of -1 is padding and selects nothing), then every dense range."""
+    """Token positions one query tile attends to: selected tiles of each segment,
+    then every dense range.  Within a segment's block of entries, -1 marks padding:
+    it and every later entry of that block select nothing (a library convention so
+    that rows of different lengths share one width; the pages define no padding)."""
     toks = []
     kc = 0
     for (st, ln, bud) in segments:
@@ -218,8 +229,8 @@ def attended_tokens(idx_row: np.ndarray, tile: int, segments: Sequence[Tuple[int
         K = min(bud, T)
         for j in idx_row[kc:kc + K]:
             j = int(j)
-            if j == -1:          # padding entry: selects nothing
-                continue
+            if j == -1:          # padding: the rest of this segment's block is unused
+                break
             if not (0 <= j < T):
                 raise ValueError("tile index out of range")
             toks.append(np.arange(st + j * tile, st + min((j + 1) * tile, ln)))
@@ -293,3 +304,48 @@ def attend(q_bits, k_bits, v_bits, idx: np.ndarray, tile: int, query: Tuple[int,
         res[(b, h, i)] = attend_tile(q_bits, k_bits, v_bits, b, h, i, idx[b, h, i], tile,
                                      query, segments, dense, scale)
     return res
+
+
+# ----------------------------------------------------------------------------- P1
+
+def window_frame_mask(n_frames: int, chunk_frames: int, halo_chunks: int,
+                      anchors: bool) -> np.ndarray:
+    """P1 at frame level: bool [F, F], entry (i, j) true when query frame i attends
+    key frame j.  Frames fall in chunks of chunk_frames consecutive frames; a chunk
+    attends itself and halo_chunks chunks on each side.  With anchors, every frame
+    also attends the first and the last frame, and those two attend every frame."""
+    if n_frames < 1 or chunk_frames < 1 or halo_chunks < 0:
+        raise ValueError("bad window pattern")
+    chunk = np.arange(n_frames) // chunk_frames
+    m = np.abs(chunk[:, None] - chunk[None, :]) <= halo_chunks
+    if anchors:
+        m[:, 0] = m[:, -1] = True
+        m[0, :] = m[-1, :] = True
+    return m
+
+
+def window_tile_rows(seg_len: int, tile: int, frame_tokens: int, chunk_frames: int,
+                     halo_chunks: int, anchors: bool) -> List[np.ndarray]:
+    """P1 at tile granularity over one segment that is both the queries and the keys:
+    for each query tile, the ascending key tiles it takes.  A tile overlaps the
+    frames its tokens belong to; query tile a takes key tile b when a frame of a
+    attends a frame of b (integer matrix product of the overlap relations)."""
+    F = -(-seg_len // frame_tokens)
+    T = -(-seg_len // tile)
+    over = np.zeros((T, F), dtype=np.int64)           # tile t overlaps frame f
+    for t, (lo, hi) in enumerate(tile_bounds(0, seg_len, tile)):
+        over[t, lo // frame_tokens:(hi - 1) // frame_tokens + 1] = 1
+    m = window_frame_mask(F, chunk_frames, halo_chunks, anchors).astype(np.int64)
+    take = (over @ m @ over.T) > 0
+    return [np.flatnonzero(take[t]).astype(np.int32) for t in range(T)]
+
+
+def window_indices(rows: Sequence[np.ndarray], width: Optional[int] = None) -> np.ndarray:
+    """Rows of P1 as one int32 [Tq, width] array, each row ascending then -1."""
+    width = max(len(r) for r in rows) if width is None else width
+    out = np.full((len(rows), width), -1, dtype=np.int32)
+    for t, r in enumerate(rows):
+        if len(r) > width:
+            raise ValueError("row longer than width")
+        out[t, :len(r)] = r
+    return out

@@ -175,3 +175,41 @@ def test_layer_attn_and_attention_checks_before_device_calls():
     Lf.budget[1] = 1008
     assert lib.veda_sparse_attn_check(ctypes.byref(Lf), fake, fake, fake, None, dense, nd, 0.0, fake) == 0
     assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, fake, dense, nd, 0.0, fake) == 0
+
+
+def _window_layer(L, tile=64, n_seg=1):
+    segs = [(0, L, 1)] if n_seg == 1 else [(0, L, 1), (L, 64, 1)]
+    return Bnd.make_layer(B=1, H=2, d=64, p=32, tile=tile, n_tokens=L + 64, query=(0, L),
+                          segments=segs, strides=((L + 64) * 128, 128, 64))
+
+
+@pytest.mark.parametrize("L,tile,ft,c,h,anchors", [
+    (1000, 64, 70, 3, 1, True), (1000, 64, 70, 3, 1, False), (640, 64, 64, 1, 0, False),
+    (640, 128, 64, 5, 1, True), (129024, 128, 4032, 5, 1, False), (350784, 128, 4032, 5, 1, True),
+    (350784, 128, 4032, 5, 1, False), (100, 64, 7, 2, 0, True),
+])
+def test_window_width_matches_oracle(L, tile, ft, c, h, anchors):
+    """The host half of the window producer: its longest row equals the oracle's."""
+    from oracle import veda_oracle as O
+    rows = O.window_tile_rows(L, tile, ft, c, h, anchors)
+    assert Bnd.window_width(_window_layer(L, tile), ft, c, h, anchors) == max(len(r) for r in rows)
+
+
+def test_window_errors_before_device_calls():
+    lib = Bnd._load()
+    fake = ctypes.c_void_p(0x10000)
+    L = _window_layer(1000)
+    with pytest.raises(Bnd.VedaError) as e:
+        Bnd.window_width(_window_layer(1000, n_seg=2), 70)
+    assert e.value.status == -2
+    Lq = _window_layer(1000)
+    Lq.query.len = 900                          # query differs from the key segment
+    assert lib.veda_window_width(ctypes.byref(Lq), 70, 5, 1, 1) == -4
+    for args in ((0, 5, 1, 1), (70, 0, 1, 1), (70, 5, -1, 1), (70, 5, 1, 2)):
+        assert lib.veda_window_width(ctypes.byref(L), *args) == -1
+    w = Bnd.window_width(L, 70, 5, 1, True)
+    T = -(-1000 // 64)
+    assert lib.veda_window_indices(ctypes.byref(L), 70, 5, 1, 1, fake, w - 1, None) == -1
+    assert lib.veda_window_indices(ctypes.byref(L), 70, 5, 1, 1, fake, T + 1, None) == -1
+    assert lib.veda_window_indices(ctypes.byref(L), 70, 5, 1, 1, None, w, None) == -1
+    assert lib.veda_window_indices(ctypes.byref(L), 70, 5, 1, 1, ctypes.c_void_p(0x10004), w, None) == -1

@@ -324,7 +324,10 @@ def _brute_mask(idx_row, tile, segments, dense, N):
         for (st, ln, bud) in segments:
             T = -(-ln // tile)
             K = min(bud, T)
-            if st <= n < st + ln and (n - st) // tile in set(int(j) for j in idx_row[kc:kc + K]):
+            blk = [int(j) for j in idx_row[kc:kc + K]]
+            if -1 in blk:                             # padding ends the segment's block
+                blk = blk[:blk.index(-1)]
+            if st <= n < st + ln and (n - st) // tile in set(blk):
                 mask[n] = True
             kc += K
         for (st, ln) in dense:
@@ -467,6 +470,24 @@ def test_padding_entries_select_nothing():
             mask[st:st + ln] = True
         ref = _sdpa_masked(qf[b, q0:q1, h], kf[b, :, h], vf[b, :, h],
                            np.broadcast_to(mask, (q1 - q0, N)).copy(), 1 / math.sqrt(d))
+        assert np.allclose(out, ref, rtol=0, atol=1e-13)
+
+
+def test_padding_ends_the_segment_block():
+    """An entry after a -1 in the same segment's block is ignored; the next segment's
+    block is read as usual (hand-written masks)."""
+    q, k, v, tile, query, segments, dense = _small_attn_layer(21)
+    segments = [(0, 14, 3), (14, 7, 2)]               # video first, three entries
+    B, N, H, d = q.shape
+    idx = np.zeros((1, H, 4, 5), dtype=np.int32)
+    idx[..., :3] = [1, -1, 2]                         # video tile 1, then padding; tile 2 unused
+    idx[..., 3:] = [-1, 0]                            # reference: padding first, tile 0 unused
+    res = O.attend(q, k, v, idx, tile, query, segments, [])
+    qf, kf, vf = (O.bf16_bits_to_f64(x) for x in (q, k, v))
+    for (b, h, i), (out, _) in res.items():
+        q0, q1 = i * tile, min((i + 1) * tile, query[1])
+        ref = _sdpa_masked(qf[b, q0:q1, h], kf[b, 4:8, h], vf[b, 4:8, h],
+                           np.ones((q1 - q0, 4), bool), 1 / math.sqrt(d))
         assert np.allclose(out, ref, rtol=0, atol=1e-13)
 
 
