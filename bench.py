@@ -240,12 +240,29 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
 def measure_patterns(lay, kernel_reps, log):
     """Other index producers through the same attention kernel: the learned selector at
     top-k budgets 16 / 32 / 64 per key segment, and the fixed VDN window pattern
-    (chunks of five latent frames, one neighbour chunk each side, boundary anchors)."""
+    (chunks of five latent frames, one neighbour chunk each side, boundary anchors);
+    each with its recall of the teacher block attention mass (random predictor
+    weights: the recall figures measure the pipeline, not a trained selector)."""
     import torch
     wl, B, I = lay.wl, lay.B, lay.I
     dev = lay.qd.device
     flops_dense = lay.dense_flops()
     out = {}
+    # teacher block attention mass (dense lse pass + per-tile mass pass over all keys)
+    mass, _, _ = B.block_mass(lay.L, lay.qd, lay.kd, lay.dense)
+    torch.cuda.synchronize()
+    log(f"[{wl.name}] teacher block mass")
+    t_ms, _, _ = time_events(lambda: B.block_mass(lay.L, lay.qd, lay.kd, lay.dense), max(2, kernel_reps // 4))
+    teacher_flops = 2 * 2.0 * wl.B * wl.H * wl.query.length * wl.d * \
+        (sum(sg.length for sg in wl.segments) + sum(r.length for r in wl.dense))
+    rec = B.block_recall(lay.L, mass, lay.idx)
+    r_ms, _, _ = time_events(lambda: B.block_recall(lay.L, mass, lay.idx), kernel_reps)
+    out["teacher"] = {"mass_ms": round(t_ms, 3), "tflops": round(teacher_flops / (t_ms * 1e-3) / 1e12, 1),
+                      "recall_ms": round(r_ms, 4), "recall_selector": round(float(rec.mean()), 4)}
+
+    def recall_of(L, idx):
+        return round(float(B.block_recall(L, mass, idx).mean()), 4)
+
     for k in (16, 32, 64):
         wk = I.with_budget(wl, k)
         Lk = B.layer_from_workload(wk)
@@ -263,7 +280,8 @@ def measure_patterns(lay, kernel_reps, log):
         fl = lay.actual_flops(idx.cpu().numpy(), [min(k, wl.seg_tiles(sg)) for sg in wl.segments])
         out[f"budget_{k}"] = {"selector_ms": round(s_ms, 4), "attn_ms": round(a_ms, 4),
                               "density": round(fl / flops_dense, 4),
-                              "actual_tflops_attn": round(fl / (a_ms * 1e-3) / 1e12, 1)}
+                              "actual_tflops_attn": round(fl / (a_ms * 1e-3) / 1e12, 1),
+                              "recall": recall_of(Lk, idx)}
         del idx, ws
     video = [s for s in wl.segments if s.name == "video"]
     if len(wl.segments) == 1 and video and video[0].start == wl.query.start \
@@ -283,8 +301,10 @@ def measure_patterns(lay, kernel_reps, log):
         out["vdn_window"] = {"chunk_frames": 5, "halo_chunks": 1, "anchors": True,
                              "width": int(Lw.budget[0]), "indices_ms": round(p_ms, 4),
                              "attn_ms": round(a_ms, 4), "density": round(fl / flops_dense, 4),
-                             "actual_tflops_attn": round(fl / (a_ms * 1e-3) / 1e12, 1)}
+                             "actual_tflops_attn": round(fl / (a_ms * 1e-3) / 1e12, 1),
+                             "recall": recall_of(Lw, idx)}
         del idx
+    del mass
     torch.cuda.synchronize()
     return out
 

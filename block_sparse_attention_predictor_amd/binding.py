@@ -91,6 +91,9 @@ def _load():
         "veda_layer_attn": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                            ctypes.POINTER(Range), ctypes.c_int32, ctypes.c_float, P, P, P,
                                            ctypes.c_size_t, P]),
+        "veda_block_mass": (ctypes.c_int, [L, P, P, ctypes.POINTER(Range), ctypes.c_int32, ctypes.c_float,
+                                           P, P, P, P]),
+        "veda_block_recall": (ctypes.c_int, [L, P, P, P, P]),
         "veda_window_width": (ctypes.c_int64, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32]),
         "veda_window_indices": (ctypes.c_int, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -109,7 +112,7 @@ def exported_symbols():
                         "veda_select_workspace_bytes", "veda_pool_project", "veda_score_topk",
                         "veda_select", "veda_sparse_attn", "veda_dequant_fp8_e4m3",
                         "veda_sparse_attn_check", "veda_layer_attn", "veda_window_width",
-                        "veda_window_indices")]
+                        "veda_window_indices", "veda_block_mass", "veda_block_recall")]
 
 
 def abi_version() -> int:
@@ -283,6 +286,36 @@ def layer_attn(layer: Layer, q, k, v, wq, wk, dense: Sequence[Tuple[int, int]] =
                                  _ptr(workspace), nbytes, _stream(stream))
     _check(st, "veda_layer_attn")
     return out, idx
+
+
+def block_mass(layer: Layer, q, k, dense: Sequence[Tuple[int, int]] = (), scale: float = 0.0,
+               want_dense: bool = True, stream=None):
+    """Teacher block attention mass fp32 [B, H, Tq, Tk] over every key tile of every segment.
+    Returns (mass, dense_mass [B, H, Tq] or None, lse [B, H, query.len])."""
+    _check_qkv(layer, q, k)
+    dev = q.device
+    mass = torch.empty((layer.B, layer.H, layer.Tq, layer.Tk), dtype=torch.float32, device=dev)
+    lse = torch.empty((layer.B, layer.H, layer.query.len), dtype=torch.float32, device=dev)
+    dm = torch.empty((layer.B, layer.H, layer.Tq), dtype=torch.float32, device=dev) if want_dense else None
+    arr, n = dense_ranges(list(dense))
+    st = _load().veda_block_mass(ctypes.byref(layer), _ptr(q), _ptr(k), arr, n, float(scale), _ptr(lse),
+                                 _ptr(mass), _ptr(dm), _stream(stream))
+    _check(st, "veda_block_mass")
+    return mass, dm, lse
+
+
+def block_recall(layer: Layer, mass, idx, stream=None):
+    """Recall fp32 [B, H, Tq] of the index set idx [B, H, Tq, Ktot] under the teacher mass."""
+    if mass.dtype != torch.float32 or tuple(mass.shape) != (layer.B, layer.H, layer.Tq, layer.Tk) \
+            or not mass.is_contiguous():
+        raise ValueError("mass must be contiguous fp32 [B, H, Tq, Tk]")
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or \
+            tuple(idx.shape) != (layer.B, layer.H, layer.Tq, layer.Ktot):
+        raise ValueError("idx must be contiguous int32 [B, H, Tq, Ktot]")
+    rec = torch.empty((layer.B, layer.H, layer.Tq), dtype=torch.float32, device=mass.device)
+    st = _load().veda_block_recall(ctypes.byref(layer), _ptr(mass), _ptr(idx), _ptr(rec), _stream(stream))
+    _check(st, "veda_block_recall")
+    return rec
 
 
 def window_width(layer: Layer, frame_tokens: int, chunk_frames: int = 5, halo_chunks: int = 1,

@@ -341,6 +341,37 @@ int veda_window_indices(const veda_layer* layer, int64_t frame_tokens, int32_t c
                                                 idx, width, (hipStream_t)stream));
 }
 
+int veda_block_mass(const veda_layer* layer, const void* q, const void* k, const veda_range* dense,
+                    int32_t n_dense, float scale, float* lse, float* mass, float* dense_mass_opt,
+                    void* stream) {
+  if (!layer) return VEDA_EINVAL;
+  veda_layer full = *layer;   // the teacher attends to every tile of every segment
+  for (int s = 0; s < full.n_seg && s < VEDA_MAX_SEGMENTS; ++s)
+    full.budget[s] = (int32_t)std::min<int64_t>(ceil_div(std::max<int64_t>(full.seg[s].len, 0),
+                                                         std::max(full.tile, 1)), INT32_MAX);
+  veda::DenseDev DD{};
+  int st = sparse_attn_check(&full, q, k, k, nullptr, dense, n_dense, scale, mass, &DD);
+  if (st != VEDA_OK) return st;
+  if (!lse || !aligned16(lse)) return VEDA_EINVAL;
+  if (dense_mass_opt && !aligned16(dense_mass_opt)) return VEDA_EINVAL;
+  LayerDev D = to_dev(&full);
+  if (D.Tq == 0) return VEDA_OK;
+  if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
+  return hip_status(veda::launch_block_mass(D, DD, q, k, scale, lse, mass, dense_mass_opt,
+                                            (hipStream_t)stream));
+}
+
+int veda_block_recall(const veda_layer* layer, const float* mass, const int32_t* idx, float* recall,
+                      void* stream) {
+  int st = check_layer(layer, false);
+  if (st != VEDA_OK) return st;
+  if (!mass || !idx || !recall) return VEDA_EINVAL;
+  if (!aligned16(mass) || !aligned16(idx) || !aligned16(recall)) return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) return VEDA_OK;
+  return hip_status(veda::launch_block_recall(D, mass, idx, recall, (hipStream_t)stream));
+}
+
 int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,
                           void* stream) {
   if (n < 0) return VEDA_EINVAL;

@@ -52,6 +52,13 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& D, const void* 
 hipError_t launch_dequant_e4m3(const uint8_t* src, void* dst, int64_t n, int32_t pow2_exp,
                                hipStream_t s);
 
+// Teacher block attention mass (two launches: dense lse, then per-tile mass) and the
+// recall of an index set under it (see block_mass.hip).  L must carry full budgets.
+hipError_t launch_block_mass(const LayerDev& L, const DenseDev& D, const void* q, const void* k,
+                             float scale, float* lse, float* mass, float* dense_mass, hipStream_t s);
+hipError_t launch_block_recall(const LayerDev& L, const float* mass, const int32_t* idx, float* recall,
+                               hipStream_t s);
+
 // Sliding frame-chunk window pattern (see patterns.hip).
 struct WindowPattern {
   int64_t frame_tokens;   // tokens per latent frame

@@ -197,6 +197,42 @@ int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const
                     void* out, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Teacher block attention mass (the full-attention pattern Veda distils its predictor
+ * from: Affine launch article, "Training the Selector, Not the Generator").  For every
+ * (b, h, query tile i) and every key tile j of every segment (all tiles, budgets are
+ * ignored), with P_n the dense softmax of query row n over ALL keys (every segment
+ * token and every dense range) at `scale` (0 selects 1/sqrt(d)):
+ *     mass[b,h,i,j]      = (1/rows_i) * sum_{n in tile i} sum_{m in tile j} P_n(m)
+ *     dense_mass[b,h,i]  = (1/rows_i) * sum_{n in tile i} sum_{m in dense ranges} P_n(m)
+ *     lse[b,h,n]         = log sum_m exp(scale * <q_n, k_m>)   (natural log)
+ * so each mass row plus its dense_mass sums to 1.  Column j runs over the key tiles
+ * of all segments in call order (segment s starts at sum_{t<s} T_t), as the score
+ * block of veda_score_topk.
+ *   q, k       : bf16 [B, N, H, d] with the layer's strides (device, 16-byte aligned).
+ *   lse        : fp32 [B, H, query.len] (output, also the second pass's input).
+ *   mass       : fp32 [B, H, Tq, Tk] (output);  dense_mass_opt: fp32 [B, H, Tq] or NULL.
+ * Two passes over all keys, bf16 matrix cores with fp32 accumulation and fp32 exp2.
+ * Same argument checks as veda_sparse_attn on the layer with full budgets.
+ * Asynchronous on `stream`; all buffers caller-owned.
+ */
+int veda_block_mass(const veda_layer* layer, const void* q, const void* k, const veda_range* dense,
+                    int32_t n_dense, float scale, float* lse, float* mass, float* dense_mass_opt,
+                    void* stream);
+
+/*
+ * Recall of an index set under the teacher mass: for every (b, h, query tile i)
+ *     recall[b,h,i] = sum of mass[b,h,i, toff_s + t] over the tiles t that idx selects
+ *                     in segment s (a -1 ends that segment's block), over all s,
+ *                     divided by sum_j mass[b,h,i,j]   (1 when that sum is 0).
+ *   mass   : fp32 [B, H, Tq, Tk] from veda_block_mass on the same segments.
+ *   idx    : int32 [B, H, Tq, Ktot] as veda_sparse_attn reads it (Ktot from the
+ *            layer's budgets); ids are not re-validated.
+ *   recall : fp32 [B, H, Tq] (output).  Device pointers, 16-byte aligned.
+ */
+int veda_block_recall(const veda_layer* layer, const float* mass, const int32_t* idx, float* recall,
+                      void* stream);
+
+/*
  * Fixed-pattern index producer: sliding windows of frame chunks with boundary
  * anchors (the VDN analysis, "The mechanism: solving instead of stepping": chunks
  * of consecutive latent frames attend to themselves and their neighbouring chunks;

@@ -25,6 +25,16 @@ layer of a video diffusion transformer):
       key range (text / VLM / audio stay dense, same record), with a two-pass
       softmax at scale 1/sqrt(d)
 
+the teacher quantity the predictor is distilled from, and how much of it a
+selection keeps:
+
+  T1  teacher block attention mass                          (Affine launch article,
+      "Training the Selector, Not the Generator": the predictor is distilled from a
+      full-attention teacher's attention patterns; at block granularity this is read
+      as the dense softmax mass that a query tile's rows put on each key tile,
+      averaged over the rows)
+  T2  recall of an index set: the selected tiles' share of the segment tiles' mass
+
 and, as a fixed index producer beside the learned one:
 
   P1  the sliding frame-chunk window with boundary anchors   (VDN article, "The
@@ -304,6 +314,75 @@ def attend(q_bits, k_bits, v_bits, idx: np.ndarray, tile: int, query: Tuple[int,
         res[(b, h, i)] = attend_tile(q_bits, k_bits, v_bits, b, h, i, idx[b, h, i], tile,
                                      query, segments, dense, scale)
     return res
+
+
+# ----------------------------------------------------------------------------- T1, T2
+
+def block_mass(q_bits, k_bits, b: int, h: int, tile: int, query: Tuple[int, int], segments,
+               dense, scale: Optional[float] = None, qtiles: Optional[Sequence[int]] = None):
+    """T1 for one (batch, head): every key of every segment and dense range is attended.
+
+    For query tile i with rows n and P_n = softmax over all keys of scale * q_n . k:
+        mass[i, j]    = (1 / rows_i) * sum_n sum_{m in key tile j} P_n(m)
+        dense_mass[i] = (1 / rows_i) * sum_n sum_{m in dense ranges} P_n(m)
+    Key tile columns run over the segments in order (segment s from sum_{t<s} T_t).
+    Returns (mass [len(qtiles), Tk], dense_mass [len(qtiles)], lse {qtile: [rows]}).
+    """
+    d = q_bits.shape[3]
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    toks, cols = [], []
+    toff = 0
+    for (st, ln, _bud) in segments:
+        t = np.arange(st, st + ln)
+        toks.append(t)
+        cols.append(toff + (t - st) // tile)
+        toff += -(-ln // tile)
+    Tk = toff
+    for (st, ln) in dense:
+        toks.append(np.arange(st, st + ln))
+        cols.append(np.full(ln, -1))
+    toks = np.concatenate(toks)
+    cols = np.concatenate(cols)
+    seg_keys = cols >= 0
+    kr = bf16_bits_to_f64(k_bits[b, toks, h, :])
+    Tq = -(-query[1] // tile)
+    qtiles = list(range(Tq)) if qtiles is None else list(qtiles)
+    mass = np.zeros((len(qtiles), Tk))
+    dmass = np.zeros(len(qtiles))
+    lses = {}
+    for r, i in enumerate(qtiles):
+        q0 = query[0] + i * tile
+        q1 = query[0] + min((i + 1) * tile, query[1])
+        qr = bf16_bits_to_f64(q_bits[b, q0:q1, h, :])
+        logits = scale * (qr @ kr.T)
+        mx = logits.max(axis=1, keepdims=True)
+        lse = mx[:, 0] + np.log(np.exp(logits - mx).sum(axis=1))
+        p = np.exp(logits - lse[:, None])
+        per_key = p.sum(axis=0) / (q1 - q0)
+        mass[r] = np.bincount(cols[seg_keys], weights=per_key[seg_keys], minlength=Tk)
+        dmass[r] = per_key[~seg_keys].sum()
+        lses[i] = lse
+    return mass, dmass, lses
+
+
+def block_recall(mass_row: np.ndarray, idx_row: np.ndarray, tile: int, segments) -> float:
+    """T2: mass of the tiles idx_row selects (segment blocks in order, a -1 ends its
+    block) over the mass of every segment tile; 1 when that total is 0."""
+    sel = 0.0
+    kc = toff = 0
+    for (st, ln, bud) in segments:
+        T = -(-ln // tile)
+        K = min(bud, T)
+        for j in idx_row[kc:kc + K]:
+            j = int(j)
+            if j == -1:
+                break
+            sel += mass_row[toff + j]
+        kc += K
+        toff += T
+    tot = float(mass_row.sum())
+    return sel / tot if tot > 0 else 1.0
 
 
 # ----------------------------------------------------------------------------- P1

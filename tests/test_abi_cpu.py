@@ -213,3 +213,26 @@ def test_window_errors_before_device_calls():
     assert lib.veda_window_indices(ctypes.byref(L), 70, 5, 1, 1, fake, T + 1, None) == -1
     assert lib.veda_window_indices(ctypes.byref(L), 70, 5, 1, 1, None, w, None) == -1
     assert lib.veda_window_indices(ctypes.byref(L), 70, 5, 1, 1, ctypes.c_void_p(0x10004), w, None) == -1
+
+
+def test_block_mass_and_recall_checks_before_device_calls():
+    lib = Bnd._load()
+    L = _layer()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10004)
+    dense, nd = Bnd.dense_ranges([(133056, 512), (133568, 256), (133824, 1024)])
+    # budgets are ignored: the teacher attends to every tile (this layer's budgets are small)
+    assert lib.veda_block_mass(ctypes.byref(L), None, fake, dense, nd, 0.0, fake, fake, None, None) == -1
+    assert lib.veda_block_mass(ctypes.byref(L), fake, fake, dense, nd, 0.0, None, fake, None, None) == -1
+    assert lib.veda_block_mass(ctypes.byref(L), fake, fake, dense, nd, 0.0, fake, None, None, None) == -1
+    assert lib.veda_block_mass(ctypes.byref(L), fake, fake, dense, nd, 0.0, fake, fake, odd, None) == -1
+    assert lib.veda_block_mass(ctypes.byref(L), fake, fake, dense, nd, -2.0, fake, fake, None, None) == -1
+    bad, nb = Bnd.dense_ranges([(133000, 100)])      # overlaps the video segment
+    assert lib.veda_block_mass(ctypes.byref(L), fake, fake, bad, nb, 0.0, fake, fake, None, None) == -4
+    assert lib.veda_block_mass(None, fake, fake, dense, nd, 0.0, fake, fake, None, None) == -1
+    Le = _layer()
+    Le.query.len = 0                                 # no query rows: nothing to do
+    assert lib.veda_block_mass(ctypes.byref(Le), fake, fake, dense, nd, 0.0, fake, fake, None, None) == 0
+    assert lib.veda_block_recall(ctypes.byref(L), None, fake, fake, None) == -1
+    assert lib.veda_block_recall(ctypes.byref(L), fake, odd, fake, None) == -1
+    assert lib.veda_block_recall(ctypes.byref(_layer(d=96)), fake, fake, fake, None) == -2
