@@ -38,6 +38,8 @@ int check_layer(const veda_layer* L, bool for_select) {
   if (L->stride_n <= 0 || L->stride_h <= 0 || L->stride_b < 0) return VEDA_EINVAL;
   if ((L->stride_b % 8) || (L->stride_n % 8) || (L->stride_h % 8)) return VEDA_EINVAL;
   if (L->stride_h < L->d) return VEDA_EINVAL;
+  // the kernels form 64-row byte offsets in 32 bits
+  if (L->stride_n >= ((int64_t)1 << 24)) return VEDA_EUNSUPPORTED;
   if (!inside(L->query, L->n_tokens)) return VEDA_ERANGE;
   int64_t tk = 0;
   for (int s = 0; s < L->n_seg; ++s) {

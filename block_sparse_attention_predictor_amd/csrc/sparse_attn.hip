@@ -24,8 +24,9 @@
 //     S^T (keys x queries)  = K . Q^T     A = K rows from LDS, B = Q^T held in VGPRs
 //     O^T (d x queries)    += V^T . P^T   A = V^T via transposing reads, B = P^T
 // Every accumulator value a lane holds then belongs to one query row
-// (lane % 32): the online softmax needs one cross-lane exchange (lane ^ 32) per
-// block, and P^T is built from S^T's accumulator registers without a shuffle
+// (lane % 32): the online softmax needs one cross-lane exchange (lane ^ 32, a
+// v_permlane32_swap) per block, and P^T is built from S^T's accumulator registers
+// without a shuffle
 // (the key order inside each 16-key slice of the O^T contraction is permuted to
 // match the accumulator layout; the V^T reads use the same permutation).
 // Softmax is fp32 in the exp2 domain with a lazily updated running maximum: the
@@ -122,10 +123,11 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   static_assert(SLOTS % NT == 0, "block split");
 
   // two stages each for K and V
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[KB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * KB * D];
+  uint16_t* const Ks0 = smem;
+  uint16_t* const Ks1 = smem + KB * D;
+  uint16_t* const Vs0 = smem + 2 * KB * D;
+  uint16_t* const Vs1 = smem + 3 * KB * D;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,16 +190,23 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     const char* g = base + blk.start * L.sn * 2;
     if (blk.n == KB) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(g + off[i]),
+      for (int i = 0; i < LPT; ++i) {
+        uint32_t o = off[i];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds((const void*)(g + o),
                                          (lds_void_t)(reinterpret_cast<char*>(dst) + (wave * LPT + i) * 1024),
                                          16, 0, 0);
+      }
     } else {
-      // partial block: rows past the end repeat the last row (masked later)
+      // partial block: rows past the end repeat the last row (masked later).  The lane
+      // id is re-read here so that nothing of this rare path stays live in registers.
+      int ln = lane;
+      asm volatile("" : "+v"(ln) : : "memory");   // also keeps this path a real branch
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        const int r = dma_row(i) < blk.n ? dma_row(i) : blk.n - 1;
-        const uint32_t o = (uint32_t)(((int64_t)r * L.sn + dma_col(i, is_v)) * 2);
+        const int r = ((wave * LPT + i) * 64 + ln) / CPR;
+        const int rc = r < blk.n ? r : blk.n - 1;
+        const uint32_t o = off[i] - (uint32_t)((r - rc) * (int)L.sn * 2);
         __builtin_amdgcn_global_load_lds((const void*)(g + o),
                                          (lds_void_t)(reinterpret_cast<char*>(dst) + (wave * LPT + i) * 1024),
                                          16, 0, 0);
@@ -215,6 +224,15 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int vg2 = (lane >> 4) & 1;
   const int vj = lane & 15;
+  // LDS byte addresses.  K operand (row l32 [+32], chunk 2kk+hi) of a block: kR ^ (kk << 5)
+  // [+ 32 rows]; the XOR swizzle only touches chunk bits, so kk enters as an XOR and the
+  // row half and the stage as plain offsets.  V^T operand (rows 16c + 8r + vrow0, columns
+  // 32db + vdcol0 ..): (vR ^ (db << 6)) + (16c + 8r) rows, likewise.
+  const uint32_t kR = (uint32_t)l32 * (D * 2) + ((uint32_t)(hi ^ swz_k<CPR>(l32)) << 4);
+  const int vrow0 = 4 * hi + (vj >> 2);
+  const int vdcol0 = 16 * vg2 + 4 * (vj & 3);
+  const uint32_t vR = (uint32_t)vrow0 * (D * 2) +
+                      ((uint32_t)((vdcol0 >> 3) ^ swz_v<CPR>(vrow0)) << 4) + (uint32_t)(vdcol0 & 7) * 2;
 
   // ---- pipeline.  Block i's K sits in Ks[i%2], its V in Vs[i%2].  In iteration i:
   //   S^T = K_i Q^T and the softmax (reads Ks[i%2])
@@ -243,26 +261,38 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
 
     // ---- S^T = K Q^T for 64 keys: two 32-key halves
     f32x16 s[2];
+    bf16x8 ka[2][D / 16];
+    const char* Kb = reinterpret_cast<const char*>(Kc);
+    uint32_t kRi = kR;   // kept in one register: the per-kk addresses are formed in the loop
+    asm volatile("" : "+v"(kRi));
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        ka[mb][kk] = *reinterpret_cast<const bf16x8*>(Kb + (kRi ^ (kk << 5)) + mb * 32 * D * 2);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
-      const int row = mb * 32 + l32;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int pc = (2 * kk + hi) ^ swz_k<CPR>(row);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kc[row * D + pc * 8]);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[kk], s[mb], 0, 0, 0);
-      }
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mb][kk], qv[kk], s[mb], 0, 0, 0);
+    // all operand reads first, then the products (the reads' latency is paid once)
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
     // ---- mask keys past the end of a partial block (tile-uniform branch)
     if (n < KB) {
+      int kb = hi * 4;                      // key = kb + c for accumulator entry (mb, e)
+      float ninf = -INFINITY;
+      asm volatile("" : "+v"(kb), "+v"(ninf) : : "memory");   // a real branch, not selects
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = mb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-          if (key >= n) s[mb][e] = -INFINITY;
+          const int c = mb * 32 + (e >> 2) * 8 + (e & 3);
+          if (kb >= n - c) s[mb][e] = ninf;
         }
     }
     // ---- online softmax, exp2 domain, lazy rescale
@@ -271,7 +301,10 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -305,6 +338,8 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     __syncthreads();
 
     // ---- V^T operands of this block, then the next DMA, then O^T += V^T P^T
+    uint32_t vRi = vR;
+    asm volatile("" : "+v"(vRi));
     bf16x8 va[D / 32][4];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -312,13 +347,9 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
       for (int c = 0; c < 4; ++c) {
         s16x4 part[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = 16 * c + 8 * r + 4 * hi + (vj >> 2);
-          const int dcol = 32 * db + 16 * vg2 + 4 * (vj & 3);
-          const int pc = (dcol >> 3) ^ swz_v<CPR>(row);
+        for (int r = 0; r < 2; ++r)
           part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t)(&Vc[row * D + pc * 8 + (dcol & 7)]));
-        }
+              (lds_s16x4_t)(reinterpret_cast<char*>(Vc) + (vRi ^ (db << 6)) + (16 * c + 8 * r) * D * 2));
         // the two halves as one 16-byte operand (whole-vector cast: building it
         // element by element through bf16 scalars is lowered wrongly by the compiler)
         const s16x8 both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -342,7 +373,8 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
 
   // ---- normalise and store (a row with no key at all, possible only when every index
   // entry is padding and there is no dense range, is written as zeros)
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (q_ok) {
     uint16_t* op = out + head_off + my_q * L.sn;

@@ -24,7 +24,7 @@
  *       elem(b, n, h, c) = base + b*stride_b + n*stride_n + h*stride_h + c
  *     (strides in elements, the head dimension c contiguous).  The natural
  *     layout is [B, n_tokens, H, d] contiguous.  Base pointers must be 16-byte
- *     aligned and the three strides multiples of 8 elements.
+ *     aligned, the three strides multiples of 8 elements and stride_n below 2^24.
  *   - Tiles: the query segment is cut into Tq = ceil(query.len / tile) tiles
  *     starting at query.start; key segment s into T_s = ceil(seg[s].len / tile)
  *     tiles starting at seg[s].start.  The last tile of a segment may be partial.
@@ -49,7 +49,7 @@ typedef enum veda_status {
   VEDA_EINVAL = -1,        /* null pointer, non-positive size, misaligned pointer or stride */
   VEDA_EUNSUPPORTED = -2,  /* d not in {64,128}, tile not in {64,128}, p not a multiple of 16
                               in [16, 256], more than VEDA_MAX_SEGMENTS / VEDA_MAX_DENSE,
-                              or more than VEDA_MAX_KEY_TILES key tiles */
+                              more than VEDA_MAX_KEY_TILES key tiles, stride_n >= 2^24 */
   VEDA_EWORKSPACE = -3,    /* workspace smaller than veda_select_workspace_bytes() */
   VEDA_ERANGE = -4,        /* a range leaves [0, n_tokens), key segments overlap each other,
                               or a dense range overlaps a key segment or another dense range */

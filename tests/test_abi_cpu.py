@@ -70,7 +70,7 @@ def test_valid_layers_pass_and_workspace_size():
 @pytest.mark.parametrize("field,value,code", [
     ("d", 96, -2), ("d", 256, -2), ("tile", 32, -2), ("p", 24, -2), ("p", 0, -2), ("p", 512, -2),
     ("B", 0, -1), ("H", 0, -1), ("n_tokens", 0, -1), ("n_seg", 5, -2), ("n_seg", 0, -1),
-    ("stride_n", 0, -1), ("stride_h", 4, -1), ("stride_n", 5124, -1),
+    ("stride_n", 0, -1), ("stride_h", 4, -1), ("stride_n", 5124, -1), ("stride_n", 1 << 24, -2),
 ])
 def test_layer_errors(field, value, code):
     assert check(_layer(**{field: value})) == code
