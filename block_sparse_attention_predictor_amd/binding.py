@@ -10,6 +10,7 @@ import ctypes
 import os
 from typing import Optional, Sequence, Tuple
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -19,7 +20,8 @@ MAX_SEGMENTS = 4
 MAX_DENSE = 8
 
 STATUS = {0: "VEDA_OK", -1: "VEDA_EINVAL", -2: "VEDA_EUNSUPPORTED", -3: "VEDA_EWORKSPACE",
-          -4: "VEDA_ERANGE", -5: "VEDA_ENOKEYS", -6: "VEDA_EHIP"}
+          -4: "VEDA_ERANGE", -5: "VEDA_ENOKEYS", -6: "VEDA_EHIP", -7: "VEDA_EIO",
+          -8: "VEDA_EFORMAT"}
 
 
 class VedaError(RuntimeError):
@@ -42,6 +44,7 @@ class Layer(ctypes.Structure):
         ("query", Range),
         ("seg", Range * MAX_SEGMENTS),
         ("budget", ctypes.c_int32 * MAX_SEGMENTS),
+        ("wdtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
     @property
@@ -94,6 +97,17 @@ def _load():
         "veda_block_mass": (ctypes.c_int, [L, P, P, ctypes.POINTER(Range), ctypes.c_int32, ctypes.c_float,
                                            P, P, P, P]),
         "veda_block_recall": (ctypes.c_int, [L, P, P, P, P]),
+        "veda_st_open": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p)]),
+        "veda_st_close": (None, [P]),
+        "veda_st_count": (ctypes.c_int64, [P]),
+        "veda_st_info": (ctypes.c_int, [P, ctypes.c_int64, ctypes.POINTER(ctypes.c_char_p),
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
+        "veda_st_find": (ctypes.c_int64, [P, ctypes.c_char_p]),
+        "veda_st_read": (ctypes.c_int, [P, ctypes.c_int64, P, ctypes.c_int64]),
+        "veda_st_metadata_count": (ctypes.c_int64, [P]),
+        "veda_st_metadata_at": (ctypes.c_int, [P, ctypes.c_int64, ctypes.POINTER(ctypes.c_char_p),
+                                               ctypes.POINTER(ctypes.c_char_p)]),
         "veda_window_width": (ctypes.c_int64, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32]),
         "veda_window_indices": (ctypes.c_int, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -112,7 +126,10 @@ def exported_symbols():
                         "veda_select_workspace_bytes", "veda_pool_project", "veda_score_topk",
                         "veda_select", "veda_sparse_attn", "veda_dequant_fp8_e4m3",
                         "veda_sparse_attn_check", "veda_layer_attn", "veda_window_width",
-                        "veda_window_indices", "veda_block_mass", "veda_block_recall")]
+                        "veda_window_indices", "veda_block_mass", "veda_block_recall",
+                        "veda_st_open", "veda_st_close", "veda_st_count", "veda_st_info",
+                        "veda_st_find", "veda_st_read", "veda_st_metadata_count",
+                        "veda_st_metadata_at")]
 
 
 def abi_version() -> int:
@@ -193,6 +210,15 @@ def _check_qkv(layer: Layer, *xs):
             raise ValueError("tensor shape differs from the layer")
 
 
+def _check_w(layer: Layer, *ws):
+    want = torch.float16 if layer.wdtype == 1 else torch.bfloat16
+    for w in ws:
+        if w.dtype != want or not w.is_cuda or not w.is_contiguous() or \
+                tuple(w.shape) != (layer.H, layer.p, layer.d):
+            raise ValueError(f"predictor weights must be contiguous {want} [H, p, d] device tensors "
+                             "(layer.wdtype selects float16 or bfloat16)")
+
+
 def select_workspace_bytes(layer: Layer) -> int:
     return _load().veda_select_workspace_bytes(ctypes.byref(layer))
 
@@ -200,6 +226,7 @@ def select_workspace_bytes(layer: Layer) -> int:
 def project(layer: Layer, q, k, wq, wk, stream=None):
     """Pooled + projected vectors (q_hat [B,H,Tq,p], k_hat [B,H,Tk,p], fp32)."""
     _check_qkv(layer, q, k)
+    _check_w(layer, wq, wk)
     dev = q.device
     qh = torch.empty((layer.B, layer.H, layer.Tq, layer.p), dtype=torch.float32, device=dev)
     kh = torch.empty((layer.B, layer.H, layer.Tk, layer.p), dtype=torch.float32, device=dev)
@@ -224,6 +251,7 @@ def select(layer: Layer, q, k, wq, wk, want_scores: bool = False, workspace=None
            stream=None):
     """Tile indices int32 [B, H, Tq, Ktot] (and fp32 scores [B, H, Tq, Tk] if asked)."""
     _check_qkv(layer, q, k)
+    _check_w(layer, wq, wk)
     dev = q.device
     if idx is None:
         idx = torch.empty((layer.B, layer.H, layer.Tq, layer.Ktot), dtype=torch.int32, device=dev)
@@ -267,6 +295,7 @@ def layer_attn(layer: Layer, q, k, v, wq, wk, dense: Sequence[Tuple[int, int]] =
     """One full layer: selection + sparse attention for the query segment, dense attention
     for every range in dense_queries.  Returns (out, idx)."""
     _check_qkv(layer, q, k, v)
+    _check_w(layer, wq, wk)
     dev = q.device
     if out is None:
         out = torch.zeros_like(q)
@@ -343,6 +372,109 @@ def window_indices(layer: Layer, frame_tokens: int, chunk_frames: int = 5, halo_
     att = Layer.from_buffer_copy(layer)
     att.budget[0] = width
     return idx, att
+
+
+# ----------------------------------------------------------------------------- predictor files
+
+ST_DTYPES = {1: ("F16", np.float16), 2: ("BF16", np.uint16), 3: ("F32", np.float32),
+             4: ("F64", np.float64), 5: ("F8_E4M3", np.uint8), 6: ("F8_E5M2", np.uint8),
+             7: ("I8", np.int8), 8: ("U8", np.uint8), 9: ("I16", np.int16), 10: ("U16", np.uint16),
+             11: ("I32", np.int32), 12: ("U32", np.uint32), 13: ("I64", np.int64),
+             14: ("U64", np.uint64), 15: ("BOOL", np.bool_)}
+
+
+class SafetensorsFile:
+    """A predictor file read through the library's native safetensors reader.  Arrays
+    come back as numpy (bf16 as uint16 bits, FP8 as uint8 codes)."""
+
+    def __init__(self, path):
+        self._lib = _load()
+        h = ctypes.c_void_p()
+        _check(self._lib.veda_st_open(os.fsencode(path), ctypes.byref(h)), f"veda_st_open({path})")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.veda_st_close(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    def __len__(self):
+        return int(self._lib.veda_st_count(self._h))
+
+    def info(self, i):
+        """(name, dtype name, shape tuple, nbytes) of tensor i (file order)."""
+        name = ctypes.c_char_p()
+        dt = ctypes.c_int32()
+        nd = ctypes.c_int32()
+        shape = (ctypes.c_int64 * 8)()
+        nb = ctypes.c_int64()
+        _check(self._lib.veda_st_info(self._h, i, ctypes.byref(name), ctypes.byref(dt), ctypes.byref(nd),
+                                      shape, ctypes.byref(nb)), "veda_st_info")
+        return name.value.decode(), ST_DTYPES[dt.value][0], tuple(shape[:nd.value]), nb.value
+
+    def names(self):
+        return [self.info(i)[0] for i in range(len(self))]
+
+    def read(self, name) -> np.ndarray:
+        i = self._lib.veda_st_find(self._h, name.encode())
+        if i < 0:
+            raise KeyError(name)
+        _, dt, shape, nb = self.info(i)
+        np_dt = dict(ST_DTYPES.values())[dt]
+        out = np.empty(shape, dtype=np_dt)
+        assert out.nbytes == nb
+        _check(self._lib.veda_st_read(self._h, i, out.ctypes.data_as(ctypes.c_void_p), nb), "veda_st_read")
+        return out
+
+    def metadata(self):
+        md = {}
+        for i in range(int(self._lib.veda_st_metadata_count(self._h))):
+            k, v = ctypes.c_char_p(), ctypes.c_char_p()
+            _check(self._lib.veda_st_metadata_at(self._h, i, ctypes.byref(k), ctypes.byref(v)),
+                   "veda_st_metadata_at")
+            md[k.value.decode()] = v.value.decode()
+        return md
+
+
+def check_selector_file(path, n_layers=50, shape=(56, 384, 128), max_bytes=560_000_000):
+    """The selector-file rules the competition publishes: exactly 2 * n_layers float16
+    tensors (query and key projection per layer), each of the given shape, and at most
+    max_bytes in total.  Returns the tensor names in file order; raises ValueError."""
+    size = os.path.getsize(path)
+    if size > max_bytes:
+        raise ValueError(f"{path}: {size} bytes exceeds {max_bytes}")
+    with SafetensorsFile(path) as f:
+        infos = [f.info(i) for i in range(len(f))]
+    if len(infos) != 2 * n_layers:
+        raise ValueError(f"{path}: {len(infos)} tensors, expected {2 * n_layers}")
+    for name, dt, shp, _ in infos:
+        if dt != "F16" or tuple(shp) != tuple(shape):
+            raise ValueError(f"{path}: tensor {name} is {dt}{list(shp)}, expected F16{list(shape)}")
+    return [i[0] for i in infos]
+
+
+def predictor_weight(f: "SafetensorsFile", name: str, device=None, pow2_exp: int = 0):
+    """One projection [H, p, d] on the device in a form the selection kernels read, and
+    its veda_wdtype: F16 and BF16 as stored; F8_E4M3 codes dequantised to bf16 on the
+    device (exact, times 2^pow2_exp)."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    arr = f.read(name)
+    _, dt, _, _ = f.info(f._lib.veda_st_find(f._h, name.encode()))
+    if dt == "F16":
+        return torch.from_numpy(arr).to(dev), 1
+    if dt == "BF16":
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev), 0
+    if dt == "F8_E4M3":
+        return dequant_fp8_e4m3(torch.from_numpy(arr).to(dev), pow2_exp), 0
+    raise ValueError(f"{name}: predictor weights must be F16, BF16 or F8_E4M3, not {dt}")
 
 
 def dequant_fp8_e4m3(codes: torch.Tensor, pow2_exp: int = 0, stream=None) -> torch.Tensor:

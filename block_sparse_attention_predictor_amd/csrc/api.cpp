@@ -32,7 +32,9 @@ int check_layer(const veda_layer* L, bool for_select) {
   if (L->B < 1 || L->H < 1 || L->n_tokens < 1) return VEDA_EINVAL;
   if (L->d != 64 && L->d != 128) return VEDA_EUNSUPPORTED;
   if (L->tile != 64 && L->tile != 128) return VEDA_EUNSUPPORTED;
-  if (for_select && (L->p < 16 || L->p > 256 || (L->p % 16) != 0)) return VEDA_EUNSUPPORTED;
+  if (for_select && (L->p < 16 || L->p > 384 || (L->p % 16) != 0)) return VEDA_EUNSUPPORTED;
+  if (L->wdtype != VEDA_W_BF16 && L->wdtype != VEDA_W_F16) return VEDA_EUNSUPPORTED;
+  if (L->reserved != 0) return VEDA_EINVAL;
   if (L->n_seg < 0 || L->n_seg > VEDA_MAX_SEGMENTS) return VEDA_EUNSUPPORTED;
   if (for_select && L->n_seg < 1) return VEDA_EINVAL;
   if (L->stride_n <= 0 || L->stride_h <= 0 || L->stride_b < 0) return VEDA_EINVAL;
@@ -77,6 +79,7 @@ LayerDev to_dev(const veda_layer* L) {
   D.sb = L->stride_b;
   D.sn = L->stride_n;
   D.sh = L->stride_h;
+  D.wdtype = L->wdtype;
   D.q0 = L->query.start;
   D.qlen = L->query.len;
   int32_t koff = 0, toff = 0;
@@ -118,6 +121,8 @@ const char* veda_status_string(int status) {
     case VEDA_ERANGE: return "token range outside the sequence or overlapping ranges";
     case VEDA_ENOKEYS: return "a query tile would attend to no key";
     case VEDA_EHIP: return "HIP launch error";
+    case VEDA_EIO: return "file could not be opened or read";
+    case VEDA_EFORMAT: return "malformed safetensors file";
     default: return "unknown status";
   }
 }

@@ -26,7 +26,7 @@ struct LayerDev {
   int32_t Tq;      // query tiles
   int32_t Tk;      // key tiles over all segments
   int32_t Ktot;    // selected tiles per query tile over all segments
-  int32_t pad_;
+  int32_t wdtype;  // predictor weight type: 0 bf16, 1 f16
   int64_t sb, sn, sh;       // element strides of q, k, v, out
   int64_t q0, qlen;         // query segment
   SegDev seg[4];

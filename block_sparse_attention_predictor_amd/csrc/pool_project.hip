@@ -12,7 +12,8 @@
 // with 16-byte loads (d/8 lanes per head row, 8 heads side by side, so a wave
 // reads whole contiguous head rows), sum in fp32 registers, combine the
 // row-parallel partial sums through LDS, divide by the number of real tokens,
-// then apply W[h] (bf16, read through L2) with fp32 dot products.
+// then apply W[h] (bf16 or f16, read through L2, converted exactly) with fp32 dot
+// products.
 #include "common.h"
 
 namespace veda {
@@ -25,8 +26,19 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// predictor weights: the low / high 16-bit element of a word as fp32 (both exact)
+template <bool F16>
+__device__ __forceinline__ float wlo(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  else return bf16lo(w);
+}
+template <bool F16>
+__device__ __forceinline__ float whi(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else return bf16hi(w);
+}
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(kThreads) void pool_project_kernel(
     LayerDev L, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk, float* __restrict__ q_hat,
@@ -133,10 +145,10 @@ __global__ __launch_bounds__(kThreads) void pool_project_kernel(
     for (int cc = 0; cc < D / 8; ++cc) {
       const uint4 w = wrow[cc];
       const float* mm = m + cc * 8;
-      s0 = fmaf(bf16lo(w.x), mm[0], s0); s1 = fmaf(bf16hi(w.x), mm[1], s1);
-      s0 = fmaf(bf16lo(w.y), mm[2], s0); s1 = fmaf(bf16hi(w.y), mm[3], s1);
-      s0 = fmaf(bf16lo(w.z), mm[4], s0); s1 = fmaf(bf16hi(w.z), mm[5], s1);
-      s0 = fmaf(bf16lo(w.w), mm[6], s0); s1 = fmaf(bf16hi(w.w), mm[7], s1);
+      s0 = fmaf(wlo<F16>(w.x), mm[0], s0); s1 = fmaf(whi<F16>(w.x), mm[1], s1);
+      s0 = fmaf(wlo<F16>(w.y), mm[2], s0); s1 = fmaf(whi<F16>(w.y), mm[3], s1);
+      s0 = fmaf(wlo<F16>(w.z), mm[4], s0); s1 = fmaf(whi<F16>(w.z), mm[5], s1);
+      s0 = fmaf(wlo<F16>(w.w), mm[6], s0); s1 = fmaf(whi<F16>(w.w), mm[7], s1);
     }
     out[(((int64_t)b * L.H + oh) * T_out + row_out) * P + oc] = s0 + s1;
   }
@@ -152,12 +164,19 @@ hipError_t launch_pool_project(const LayerDev& L, const void* q, const void* k, 
   auto kk = static_cast<const uint16_t*>(k);
   auto wqq = static_cast<const uint16_t*>(wq);
   auto wkk = static_cast<const uint16_t*>(wk);
-  if (L.d == 128)
-    hipLaunchKernelGGL(pool_project_kernel<128>, grid, dim3(kThreads), 0, s, L, qq, kk, wqq, wkk,
-                       q_hat, k_hat);
+  const bool f16 = L.wdtype == 1;
+  if (L.d == 128 && f16)
+    hipLaunchKernelGGL((pool_project_kernel<128, true>), grid, dim3(kThreads), 0, s, L, qq, kk, wqq,
+                       wkk, q_hat, k_hat);
+  else if (L.d == 128)
+    hipLaunchKernelGGL((pool_project_kernel<128, false>), grid, dim3(kThreads), 0, s, L, qq, kk, wqq,
+                       wkk, q_hat, k_hat);
+  else if (f16)
+    hipLaunchKernelGGL((pool_project_kernel<64, true>), grid, dim3(kThreads), 0, s, L, qq, kk, wqq,
+                       wkk, q_hat, k_hat);
   else
-    hipLaunchKernelGGL(pool_project_kernel<64>, grid, dim3(kThreads), 0, s, L, qq, kk, wqq, wkk,
-                       q_hat, k_hat);
+    hipLaunchKernelGGL((pool_project_kernel<64, false>), grid, dim3(kThreads), 0, s, L, qq, kk, wqq,
+                       wkk, q_hat, k_hat);
   return hipGetLastError();
 }
 

@@ -105,12 +105,19 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
         buf[ks][1] = ok ? *reinterpret_cast<const float4*>(krow + c0 + 4) : make_float4(0, 0, 0, 0);
       }
     };
-    float4 cur[kMaxKSteps][2], nxt[kMaxKSteps][2];
+    // up to 256 predictor columns the next column block is prefetched; beyond that the
+    // two buffers would not fit the register file, so each block is loaded in place
+    constexpr bool kPrefetch = kMaxKSteps <= 8;
+    float4 cur[kMaxKSteps][2], nxt[kPrefetch ? kMaxKSteps : 1][2];
     int cb = wave;
-    if (cb * 16 < Tk) load_b(cb, cur);
+    if (kPrefetch && cb * 16 < Tk) load_b(cb, cur);
     for (; cb * 16 < Tk; cb += kWaves) {
       const int cb_next = cb + kWaves;
-      if (cb_next * 16 < Tk) load_b(cb_next, nxt);
+      if constexpr (kPrefetch) {
+        if (cb_next * 16 < Tk) load_b(cb_next, nxt);
+      } else {
+        load_b(cb, cur);
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kMaxKSteps; ++ks) {
@@ -134,10 +141,12 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
           if (scores) scores[(bh * L.Tq + row0 + r) * Tk + kcol] = acc[j];
         }
       }
+      if constexpr (kPrefetch) {
 #pragma unroll
-      for (int ks = 0; ks < kMaxKSteps; ++ks) {
-        cur[ks][0] = nxt[ks][0];
-        cur[ks][1] = nxt[ks][1];
+        for (int ks = 0; ks < kMaxKSteps; ++ks) {
+          cur[ks][0] = nxt[ks][0];
+          cur[ks][1] = nxt[ks][1];
+        }
       }
     }
   }
@@ -254,7 +263,7 @@ hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float*
   const int R = score_rows_per_block(L.Tk);
   const size_t lds = (size_t)R * L.Tk * 4 + kWaves * kHistCopies * 256 * 4;
   dim3 grid((unsigned)((L.Tq + R - 1) / R), (unsigned)L.H, (unsigned)L.B);
-  // the kernel is instantiated for 32-wide predictor steps: p <= 64, 128, 256
+  // the kernel is instantiated for 32-wide predictor steps: p <= 64, 128, 256, 384
   auto run = [&](auto kern) -> hipError_t {
     if (lds > 64 * 1024) {
       hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -269,8 +278,10 @@ hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float*
     e = run(score_topk_kernel<2>);
   else if (L.p <= 128)
     e = run(score_topk_kernel<4>);
-  else
+  else if (L.p <= 256)
     e = run(score_topk_kernel<8>);
+  else
+    e = run(score_topk_kernel<12>);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

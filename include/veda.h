@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 1
+#define VEDA_ABI_VERSION 2
 #define VEDA_MAX_SEGMENTS 4
 #define VEDA_MAX_DENSE 8
 #define VEDA_MAX_KEY_TILES 8192   /* sum over segments of T_s accepted by selection */
@@ -48,13 +48,15 @@ typedef enum veda_status {
   VEDA_OK = 0,
   VEDA_EINVAL = -1,        /* null pointer, non-positive size, misaligned pointer or stride */
   VEDA_EUNSUPPORTED = -2,  /* d not in {64,128}, tile not in {64,128}, p not a multiple of 16
-                              in [16, 256], more than VEDA_MAX_SEGMENTS / VEDA_MAX_DENSE,
+                              in [16, 384], more than VEDA_MAX_SEGMENTS / VEDA_MAX_DENSE,
                               more than VEDA_MAX_KEY_TILES key tiles, stride_n >= 2^24 */
   VEDA_EWORKSPACE = -3,    /* workspace smaller than veda_select_workspace_bytes() */
   VEDA_ERANGE = -4,        /* a range leaves [0, n_tokens), key segments overlap each other,
                               or a dense range overlaps a key segment or another dense range */
   VEDA_ENOKEYS = -5,       /* a query tile would attend to no key at all */
-  VEDA_EHIP = -6           /* the HIP runtime reported an error at launch */
+  VEDA_EHIP = -6,          /* the HIP runtime reported an error at launch */
+  VEDA_EIO = -7,           /* a file could not be opened or read */
+  VEDA_EFORMAT = -8        /* a file is not a well-formed safetensors file */
 } veda_status;
 
 /* Token range [start, start + len). */
@@ -62,6 +64,12 @@ typedef struct veda_range {
   int64_t start;
   int64_t len;
 } veda_range;
+
+/* Element type of the predictor weights Wq, Wk. */
+typedef enum veda_wdtype {
+  VEDA_W_BF16 = 0,         /* bfloat16 (also the result of veda_dequant_fp8_e4m3) */
+  VEDA_W_F16 = 1           /* IEEE float16, as the competition's selector files store them */
+} veda_wdtype;
 
 /* Shape of one attention layer. */
 typedef struct veda_layer {
@@ -78,6 +86,8 @@ typedef struct veda_layer {
   veda_range seg[VEDA_MAX_SEGMENTS];      /* key segments, in call order          */
   int32_t budget[VEDA_MAX_SEGMENTS];      /* top-k budget per segment, >= 0; a budget
                                              above T_s selects every tile          */
+  int32_t wdtype;     /* veda_wdtype of Wq, Wk (selection only); 0 = bf16          */
+  int32_t reserved;   /* must be 0                                                */
 } veda_layer;
 
 /* Ktot = sum_s min(budget[s], T_s): index entries per (b, h, query tile). */
@@ -107,7 +117,8 @@ size_t veda_select_workspace_bytes(const veda_layer* layer);
  * likewise k_hat[b, h, j, :] = Wk[h] k_bar[j] for every tile j of every key
  * segment, segments concatenated in call order.
  *   q, k   : bf16, strided as described above
- *   wq, wk : bf16 [H, p, d] contiguous, 16-byte aligned
+ *   wq, wk : [H, p, d] contiguous, 16-byte aligned, bf16 or f16 (layer->wdtype);
+ *            both types convert to fp32 exactly
  *   q_hat  : fp32 [B, H, Tq, p] contiguous (output)
  *   k_hat  : fp32 [B, H, sum_s T_s, p] contiguous (output)
  */
@@ -268,6 +279,39 @@ int veda_window_indices(const veda_layer* layer, int64_t frame_tokens, int32_t c
  */
 int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,
                           void* stream);
+
+/*
+ * safetensors reader (host only) for predictor files: the competition's selector
+ * file holds float16 query/key projections per layer (Affine launch article, "How
+ * the SN120 Competition Works"); the R2VA predictor is stored in FP8 and turned into
+ * bf16 at load (Veda R2VA record, first paragraph; veda_dequant_fp8_e4m3 does that on
+ * the device).  Layout: 8-byte little-endian header length, a JSON header mapping
+ * names to {dtype, shape, data_offsets} plus an optional "__metadata__" string map,
+ * then the data.  veda_st_open checks the whole header (offsets inside the file,
+ * byte counts = dtype size x shape, the tensors tiling the data without holes or
+ * overlap) and returns VEDA_EIO (cannot open/read) or VEDA_EFORMAT (malformed).
+ * Names, metadata strings and the handle stay valid until veda_st_close.  Tensors
+ * keep the file's order.  veda_st_read copies a tensor's raw little-endian bytes into
+ * host memory of exactly veda_st_info's nbytes.
+ */
+typedef struct veda_st_file veda_st_file;
+typedef enum veda_st_dtype {
+  VEDA_ST_UNKNOWN = 0, VEDA_ST_F16 = 1, VEDA_ST_BF16 = 2, VEDA_ST_F32 = 3, VEDA_ST_F64 = 4,
+  VEDA_ST_F8_E4M3 = 5, VEDA_ST_F8_E5M2 = 6, VEDA_ST_I8 = 7, VEDA_ST_U8 = 8, VEDA_ST_I16 = 9,
+  VEDA_ST_U16 = 10, VEDA_ST_I32 = 11, VEDA_ST_U32 = 12, VEDA_ST_I64 = 13, VEDA_ST_U64 = 14,
+  VEDA_ST_BOOL = 15
+} veda_st_dtype;
+#define VEDA_ST_MAX_DIMS 8
+int veda_st_open(const char* path, veda_st_file** out);
+void veda_st_close(veda_st_file* file);
+int64_t veda_st_count(const veda_st_file* file);
+int veda_st_info(const veda_st_file* file, int64_t i, const char** name, int32_t* dtype,
+                 int32_t* ndim, int64_t* shape /* [VEDA_ST_MAX_DIMS] */, int64_t* nbytes);
+/* index of the tensor called name, or VEDA_ERANGE when there is none */
+int64_t veda_st_find(const veda_st_file* file, const char* name);
+int veda_st_read(const veda_st_file* file, int64_t i, void* dst_host, int64_t nbytes);
+int64_t veda_st_metadata_count(const veda_st_file* file);
+int veda_st_metadata_at(const veda_st_file* file, int64_t i, const char** key, const char** value);
 
 #ifdef __cplusplus
 }

@@ -175,10 +175,13 @@ def topk_lowest_index(row: np.ndarray, k: int) -> np.ndarray:
 # ----------------------------------------------------------------------------- selection
 
 def weights_f64(w) -> np.ndarray:
-    """Predictor weights as float64 [H, p, d] from bf16 bits (uint16) or FP8 bytes."""
+    """Predictor weights as float64 [H, p, d]: bf16 bits (uint16), IEEE float16 values
+    (numpy float16, converted exactly), or FP8 bytes as (codes, pow2_exp)."""
     if isinstance(w, tuple):  # (codes, pow2_exp)
         codes, e = w
         return dequant_e4m3fn(codes, e)
+    if w.dtype == np.float16:
+        return w.astype(np.float64)
     return bf16_bits_to_f64(w)
 
 

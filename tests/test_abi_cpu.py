@@ -37,8 +37,8 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert Bnd.abi_version() == 1
-    for code in range(-6, 1):
+    assert Bnd.abi_version() == 2
+    for code in range(-8, 1):
         assert Bnd.status_string(code) and "unknown" not in Bnd.status_string(code)
     assert "unknown" in Bnd.status_string(-99)
 
@@ -71,6 +71,7 @@ def test_valid_layers_pass_and_workspace_size():
     ("d", 96, -2), ("d", 256, -2), ("tile", 32, -2), ("p", 24, -2), ("p", 0, -2), ("p", 512, -2),
     ("B", 0, -1), ("H", 0, -1), ("n_tokens", 0, -1), ("n_seg", 5, -2), ("n_seg", 0, -1),
     ("stride_n", 0, -1), ("stride_h", 4, -1), ("stride_n", 5124, -1), ("stride_n", 1 << 24, -2),
+    ("p", 400, -2), ("p", 384, 0), ("wdtype", 2, -2), ("wdtype", 1, 0), ("reserved", 1, -1),
 ])
 def test_layer_errors(field, value, code):
     assert check(_layer(**{field: value})) == code

@@ -504,3 +504,14 @@ def test_dense_query_rows_match_sdpa():
         vt = torch.from_numpy(vf[0, keys, h])[None, None]
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0].numpy()
         assert np.allclose(out, ref, rtol=0, atol=1e-13)
+
+
+def test_float16_weights_are_exact():
+    """IEEE float16 predictor weights enter the oracle as their exact values."""
+    w = np.array([65504.0, -2.0 ** -24, 2.0 ** -14, 1 + 2.0 ** -10, -0.0, 0.333], dtype=np.float16)
+    got = O.weights_f64(w)
+    assert got.dtype == np.float64
+    assert got[:5].tolist() == [65504.0, -2.0 ** -24, 2.0 ** -14, 1 + 2.0 ** -10, 0.0]
+    assert math.copysign(1.0, got[4]) == -1.0
+    assert got[5] == 0.333 + (float(np.float16(0.333)) - 0.333)     # the float16 value itself
+    assert got[5] != 0.333
