@@ -17,8 +17,9 @@
 //   pass 1: S^T = K Q^T on v_mfma_f32_32x32x16_bf16, running max and sum in the exp2
 //           domain -> lse_n (fp32);
 //   pass 2: the same product, p = exp2(s - lse_n), summed per lane, across the wave
-//           and across the waves (one LDS slot per wave and block, read after the
-//           pipeline's barrier) -> one value per key tile, stored by wave 0.
+//           (DPP row rotations and lane swaps, no LDS) and across the waves (one LDS
+//           slot per wave and block, read after the pipeline's barrier) -> one value
+//           per key tile, stored by wave 0.
 #include "common.h"
 
 #include <type_traits>
@@ -69,10 +70,21 @@ struct KeyWalk {
 template <int CPR>
 __device__ __forceinline__ int swz_k(int row) { return row & (CPR - 1); }
 
+// Sum over the 64 lanes without LDS: rotations within each 16-lane row (DPP), then
+// the row pairs (lane ^ 16) and the halves (lane ^ 32) through lane swaps.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x120 + N, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int D, int NW, bool MASS>
@@ -86,9 +98,10 @@ __global__ __launch_bounds__(64 * NW, 2) void block_mass_kernel(
   constexpr int LPT = SLOTS / NT;
   static_assert(SLOTS % NT == 0, "block split");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * KB * D];
   __shared__ float red[2][NW];
+  uint16_t* const Ks0 = smem;
+  uint16_t* const Ks1 = smem + KB * D;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -141,15 +154,21 @@ __global__ __launch_bounds__(64 * NW, 2) void block_mass_kernel(
     const char* g = kbase + blk.start * L.sn * 2;
     if (blk.n == KB) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(g + koff[i]),
+      for (int i = 0; i < LPT; ++i) {
+        uint32_t o = koff[i];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds((const void*)(g + o),
                                          (lds_void_t)(reinterpret_cast<char*>(dst) + (wave * LPT + i) * 1024),
                                          16, 0, 0);
+      }
     } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln) : : "memory");
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        const int r = dma_row(i) < blk.n ? dma_row(i) : blk.n - 1;
-        const uint32_t o = (uint32_t)(((int64_t)r * L.sn + dma_col(i)) * 2);
+        const int r = ((wave * LPT + i) * 64 + ln) / CPR;
+        const int rc = r < blk.n ? r : blk.n - 1;
+        const uint32_t o = koff[i] - (uint32_t)((r - rc) * (int)L.sn * 2);
         __builtin_amdgcn_global_load_lds((const void*)(g + o),
                                          (lds_void_t)(reinterpret_cast<char*>(dst) + (wave * LPT + i) * 1024),
                                          16, 0, 0);
@@ -157,6 +176,8 @@ __global__ __launch_bounds__(64 * NW, 2) void block_mass_kernel(
     }
   };
 
+  // K operand (row l32 [+32], chunk 2kk+hi) of a block: kR ^ (kk << 5) [+ 32 rows]
+  const uint32_t kR = (uint32_t)l32 * (D * 2) + ((uint32_t)(hi ^ swz_k<CPR>(l32)) << 4);
   float m_run = -INFINITY, l_run = 0.f;   // pass 1
   float acc = 0.f, dacc = 0.f;            // pass 2 (wave 0): current tile, dense ranges
   const int rows = (int)((q_end - q_first) < L.tile ? (q_end - q_first) : L.tile);
@@ -177,25 +198,36 @@ __global__ __launch_bounds__(64 * NW, 2) void block_mass_kernel(
     uint16_t* Kc = ST ? Ks1 : Ks0;
     const int n = b0.n;
     f32x16 s[2];
+    bf16x8 ka[2][D / 16];
+    const char* Kb = reinterpret_cast<const char*>(Kc);
+    uint32_t kRi = kR;   // one register; the per-kk addresses are formed here
+    asm volatile("" : "+v"(kRi));
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        ka[mb][kk] = *reinterpret_cast<const bf16x8*>(Kb + (kRi ^ (kk << 5)) + mb * 32 * D * 2);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
-      const int row = mb * 32 + l32;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int pc = (2 * kk + hi) ^ swz_k<CPR>(row);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kc[row * D + pc * 8]);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[kk], s[mb], 0, 0, 0);
-      }
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mb][kk], qv[kk], s[mb], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
     if (n < KB) {
+      int kb = hi * 4;                      // key = kb + c for accumulator entry (mb, e)
+      float ninf = -INFINITY;
+      asm volatile("" : "+v"(kb), "+v"(ninf) : : "memory");
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = mb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-          if (key >= n) s[mb][e] = -INFINITY;
+          const int c = mb * 32 + (e >> 2) * 8 + (e & 3);
+          if (kb >= n - c) s[mb][e] = ninf;
         }
     }
     if constexpr (!MASS) {
@@ -204,7 +236,8 @@ __global__ __launch_bounds__(64 * NW, 2) void block_mass_kernel(
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
         const float m_new = fmaxf(m_run, mx);
         l_run *= __builtin_amdgcn_exp2f(m_run - m_new);
@@ -256,7 +289,8 @@ __global__ __launch_bounds__(64 * NW, 2) void block_mass_kernel(
   }
 
   if constexpr (!MASS) {
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     if (q_ok && hi == 0)
       lse[(int64_t)bh * L.qlen + (my_q - L.q0)] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
   } else {

@@ -7,7 +7,7 @@
 // pattern is produced at tile granularity for the block-sparse attention call: a
 // query tile takes every key tile that overlaps the key frames of any of its query
 // frames.  Rows have different lengths; they are written ascending and padded with
-// -1 to a common width (the attention kernel skips -1 entries).
+// -1 to a common width (a -1 ends the row's block for the attention kernel).
 #include "common.h"
 
 namespace veda {
@@ -71,20 +71,32 @@ __host__ __device__ inline int window_intervals(int64_t q0, int64_t qlen, int64_
 
 namespace {
 
+// One wave per (b*h, query tile) row: the row's intervals are computed once per lane,
+// then the 64 lanes write consecutive entries (coalesced), -1 past the row's length.
 __global__ __launch_bounds__(256) void window_indices_kernel(int64_t q0, int64_t qlen, int64_t tile,
                                                              int64_t seg_len, int32_t Tq, int32_t BH,
                                                              WindowPattern P, int32_t* __restrict__ idx,
                                                              int32_t kmax) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one (b*h, query tile) per thread
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (g >= (int64_t)BH * Tq) return;
   const int qt = (int)(g % Tq);
   int64_t lo[3], hi[3];
   const int n = window_intervals(q0, qlen, tile, seg_len, qt, P, lo, hi);
+  int64_t len[3] = {0, 0, 0};
+  for (int i = 0; i < n; ++i) len[i] = hi[i] - lo[i] + 1;
   int32_t* row = idx + g * kmax;
-  int w = 0;
-  for (int i = 0; i < n; ++i)
-    for (int64_t t = lo[i]; t <= hi[i] && w < kmax; ++t) row[w++] = (int32_t)t;
-  for (; w < kmax; ++w) row[w] = -1;
+  for (int64_t w = lane; w < kmax; w += 64) {
+    int64_t r = w, v = -1;
+    for (int i = 0; i < n; ++i) {
+      if (r < len[i]) {
+        v = lo[i] + r;
+        break;
+      }
+      r -= len[i];
+    }
+    row[w] = (int32_t)v;
+  }
 }
 
 }  // namespace
@@ -106,7 +118,8 @@ hipError_t launch_window_indices(int64_t q0, int64_t qlen, int64_t tile, int64_t
                                  int32_t BH, const WindowPattern& P, int32_t* idx, int32_t kmax,
                                  hipStream_t s) {
   const int64_t n = (int64_t)BH * Tq;
-  hipLaunchKernelGGL(window_indices_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, q0, qlen,
+  if ((n + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(window_indices_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, q0, qlen,
                      tile, seg_len, Tq, BH, P, idx, kmax);
   return hipGetLastError();
 }
