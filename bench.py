@@ -41,8 +41,8 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time selection + attention on every workload (field 'sweep')")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip timing selection + attention on every workload (field 'sweep')")
     ap.add_argument("--no-patterns", action="store_true",
                     help="skip the budget 16/32/64 and VDN window timings (field 'patterns')")
     ap.add_argument("--calib-copy", action="store_true",
@@ -408,7 +408,7 @@ def main():
         also = res2
         del lay2
     sweep = None
-    if args.sweep:
+    if not args.no_sweep:
         sweep = {}
         for name in ("tiny", "mid", "t2v5s", "r2va", "t2v14s"):
             if name == args.workload:
@@ -417,7 +417,7 @@ def main():
                 lay_s, r = measure(name, max(3, args.steps // 2), 1, args.kernel_reps, args.dense_reps,
                                    False, log)
                 del lay_s
-            sweep[name] = {k: round(r[k], 4) for k in ("ms_per_step", "selector_ms", "attn_ms",
+            sweep[name] = {k: round(r[k], 4) for k in ("ms_per_step", "selector_ms", "attn_ms", "full_layer_ms",
                                                        "actual_tflops_attn", "dense_equiv_tflops_step",
                                                        "sparsity_actual")}
             import torch
