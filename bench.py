@@ -159,6 +159,59 @@ def time_events(fn, reps):
     return float(np.mean(times)), float(np.min(times)), float(np.median(times))
 
 
+def index_stats(wl, idx_np):
+    """Selection statistics per head (video segment): mean Jaccard overlap of neighbouring
+    query tiles' index sets, and the number of distinct key tiles a head selects."""
+    col = 0
+    for s in wl.segments:
+        K = min(s.budget, wl.seg_tiles(s))
+        if s.name == "video":
+            break
+        col += K
+    sel = idx_np[0, :, :, col:col + K]                     # [H, Tq, K]
+    H, Tq, _ = sel.shape
+    T = wl.seg_tiles([s for s in wl.segments if s.name == "video"][0])
+    onehot = np.zeros((H, Tq, T), dtype=bool)
+    np.put_along_axis(onehot, sel.astype(np.int64), True, axis=-1)
+    inter = (onehot[:, 1:] & onehot[:, :-1]).sum(-1)
+    union = (onehot[:, 1:] | onehot[:, :-1]).sum(-1)
+    jac = (inter / np.maximum(union, 1)).mean(axis=1)     # [H]
+    distinct = onehot.any(axis=1).sum(-1)                  # [H]
+    return {"jaccard_neighbour_mean": round(float(jac.mean()), 4),
+            "jaccard_neighbour_min_head": round(float(jac.min()), 4),
+            "distinct_tiles_per_head_mean": round(float(distinct.mean()), 1), "tiles": int(T)}
+
+
+def device_peaks(log):
+    """What this device reaches on an MFMA-only loop and on a plain 1 GiB copy."""
+    import torch
+    B = __import__("block_sparse_attention_predictor_amd.binding", fromlist=["x"])
+    B.mfma_peak(50, 2048)
+    torch.cuda.synchronize()
+    ms, _, _ = time_events(lambda: B.mfma_peak(2000, 2048), 3)
+    _, flops = B.mfma_peak(1, 1)
+    flops *= 2000 * 2048
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    cms, _, _ = time_events(lambda: dst.copy_(src), 5)
+    del src, dst
+    out = {"mfma_bf16_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "copy_gbs": round(2.0 * n * 2 / (cms * 1e-3) / 1e9, 1)}
+    log(f"device peaks: {out}")
+    return out
+
+
+def environment():
+    import platform
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__, "host": platform.node()}
+
+
 def copy_calibration():
     """A plain device copy of known size (1 GiB read + 1 GiB written), run once so that
     hardware byte counters can be scaled against it in a profiled run."""
@@ -223,6 +276,30 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
     # pooling bandwidth: Q rows of the query segment + K rows of every key segment, once
     pool_bytes = 2.0 * wl.B * wl.H * wl.d * (wl.query.length + sum(sg.length for sg in wl.segments))
     res["pool_bytes"] = pool_bytes
+    pool_mean, pool_min, pool_med = time_events(
+        lambda: lay.B.project(lay.L, lay.qd, lay.kd, lay.wq, lay.wk), kernel_reps)
+    res["pool_ms"] = pool_mean
+    res["pool_gbs"] = pool_bytes / (pool_med * 1e-3) / 1e9
+    res["selector_ms_median"] = float(np.median(sel_ms))
+    res["attn_ms_median"] = float(np.median(att_ms))
+    res["index_stats"] = index_stats(wl, idx_np)
+    # cold caches: a 512 MiB write before every step flushes the Infinity Cache and L2
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=lay.qd.device)
+    cold_sel, cold_att = [], []
+    for _ in range(max(3, min(steps, 5))):
+        flush.fill_(1.0)
+        c = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        c[0].record()
+        lay.select()
+        c[1].record()
+        lay.attn()
+        c[2].record()
+        c[2].synchronize()
+        cold_sel.append(c[0].elapsed_time(c[1]))
+        cold_att.append(c[1].elapsed_time(c[2]))
+    res["cold"] = {"selector_ms_median": float(np.median(cold_sel)), "attn_ms_median": float(np.median(cold_att)),
+                   "selector_ms_min": float(np.min(cold_sel)), "attn_ms_min": float(np.min(cold_att))}
+    del flush
     if with_dense:
         Lf, wlf = lay.full_budget_layer()
         idx_full = torch.from_numpy(lay.I.full_indices(wl)).to(lay.qd.device)
@@ -234,6 +311,10 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
         res["dense_tflops"] = flops_dense / (d_mean * 1e-3) / 1e12
         res["speedup_vs_dense"] = d_mean / ms_step
         del idx_full
+        res["sdpa_dense"] = sdpa_dense(lay, dense_reps, log)
+        if "ms_median" in res["sdpa_dense"]:
+            # the speedup is claimed against the faster of the two dense baselines
+            res["speedup_vs_fastest_dense"] = min(d_mean, res["sdpa_dense"]["ms_median"]) / ms_step
     return lay, res
 
 
@@ -309,6 +390,54 @@ def measure_patterns(lay, kernel_reps, log):
     return out
 
 
+def random_pattern(lay, kernel_reps, log):
+    """Uniformly random index sets of the same budgets: the worst case for K/V reuse."""
+    import torch
+    wl = lay.wl
+    idx = torch.from_numpy(lay.I.random_indices(wl)).to(lay.qd.device)
+    lay.attn(idx)
+    torch.cuda.synchronize()
+    ms, _, med = time_events(lambda: lay.attn(idx), kernel_reps)
+    fl = lay.actual_flops(idx.cpu().numpy())
+    log(f"[{wl.name}] random index sets: {med:.3f} ms")
+    return {"attn_ms": round(ms, 4), "attn_ms_median": round(med, 4),
+            "actual_tflops_attn": round(fl / (med * 1e-3) / 1e12, 1)}
+
+
+def sdpa_dense(lay, reps, log):
+    """torch's scaled_dot_product_attention (flash / memory-efficient backends only) at the
+    dense shape of the layer, every token a key: context for the dense baseline."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    wl = lay.wl
+    q0, nq = wl.query.start, wl.query.length
+    try:
+        qh = lay.qd[:, q0:q0 + nq].transpose(1, 2).contiguous()
+        kh = lay.kd.transpose(1, 2).contiguous()
+        vh = lay.vd.transpose(1, 2).contiguous()
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            torch.nn.functional.scaled_dot_product_attention(qh, kh, vh)
+            torch.cuda.synchronize()
+            ms, _, med = time_events(lambda: torch.nn.functional.scaled_dot_product_attention(qh, kh, vh), reps)
+        del qh, kh, vh
+        flops = 4.0 * wl.B * wl.H * nq * wl.n_tokens * wl.d
+        log(f"[{wl.name}] torch SDPA dense: {med:.1f} ms")
+        return {"ms": round(ms, 3), "ms_median": round(med, 3), "tflops": round(flops / (med * 1e-3) / 1e12, 1)}
+    except Exception as e:   # a backend missing on this build is reported, not fatal
+        return {"error": f"{type(e).__name__}: {str(e)[:200]}"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(lay, log, budget_s=20.0):
     """The fp64 oracle on a bounded sample of the same layer (about budget_s of CPU
     work), extrapolated to the whole layer."""
@@ -361,7 +490,7 @@ def cpu_baseline(lay, log, budget_s=20.0):
                    f"{t_sel:.1f} s; attention on {len(pairs)} random (head, query tile) pairs in {t_att:.1f} s; "
                    f"extrapolated to the whole layer: {layer_s:.0f} s per layer"),
         "layer_s_extrapolated": layer_s,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": _cpu_model() or platform.processor() or platform.machine(),
     }
 
 
@@ -401,6 +530,9 @@ def main():
                        not args.no_dense, log)
     wl = lay.wl
     patterns = None if args.no_patterns else measure_patterns(lay, args.kernel_reps, log)
+    if patterns is not None:
+        patterns["random_indices"] = random_pattern(lay, args.kernel_reps, log)
+    peaks = device_peaks(log)
     also = None
     if args.also and args.also != "none" and args.also != args.workload:
         lay2, res2 = measure(args.also, args.steps, args.warmup, args.kernel_reps, args.dense_reps,
@@ -452,6 +584,20 @@ def main():
         "mfma_util": round(achieved / PEAK_BF16_TFLOPS, 4),
         "dense_ms": round(res.get("dense_ms", float("nan")), 3) if "dense_ms" in res else None,
         "speedup_vs_dense": round(res["speedup_vs_dense"], 2) if "speedup_vs_dense" in res else None,
+        "mfma_util_vs_measured_peak": round(achieved / peaks["mfma_bf16_tflops"], 4),
+        "selector_ms_median": round(res["selector_ms_median"], 4),
+        "attn_ms_median": round(res["attn_ms_median"], 4),
+        "cold": {k: round(v, 4) for k, v in res["cold"].items()},
+        "pool": {"ms": round(res["pool_ms"], 4), "gbs": round(res["pool_gbs"], 1),
+                 "frac_hbm_peak": round(res["pool_gbs"] / PEAK_HBM_GBS, 4),
+                 "frac_copy": round(res["pool_gbs"] / peaks["copy_gbs"], 4),
+                 "bytes": res["pool_bytes"]},
+        "index_stats": res["index_stats"],
+        "sdpa_dense": res.get("sdpa_dense"),
+        "speedup_vs_fastest_dense": round(res["speedup_vs_fastest_dense"], 2)
+        if "speedup_vs_fastest_dense" in res else None,
+        "device_peaks": peaks,
+        "env": environment(),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": (round(traffic / 1e9, 2) if traffic else None),

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libveda.so")
 SOURCES = ["api.cpp", "dequant.hip", "pool_project.hip", "score_topk.hip", "sparse_attn.hip",
-           "patterns.hip", "block_mass.hip", "safetensors.cpp"]
+           "patterns.hip", "block_mass.hip", "safetensors.cpp", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -379,6 +379,11 @@ int veda_block_recall(const veda_layer* layer, const float* mass, const int32_t*
   return hip_status(veda::launch_block_recall(D, mass, idx, recall, (hipStream_t)stream));
 }
 
+int veda_mfma_peak(float* out, int32_t iters, int32_t workgroups, void* stream) {
+  if (!out || iters < 1 || workgroups < 1) return VEDA_EINVAL;
+  return hip_status(veda::launch_mfma_peak(out, iters, workgroups, (hipStream_t)stream));
+}
+
 int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,
                           void* stream) {
   if (n < 0) return VEDA_EINVAL;

@@ -281,6 +281,16 @@ int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t
                           void* stream);
 
 /*
+ * Measurement aid (not part of the method): an MFMA-only loop, so that the attention
+ * kernel's matrix-core use can be reported against the rate this device actually
+ * reaches as well as against the specification.  Each of `workgroups` workgroups of
+ * 256 threads runs iters x 16 products of v_mfma_f32_32x32x16_bf16 per wave
+ * (32768 flops each): 2,097,152 * iters * workgroups flops in total.  out: fp32 device
+ * buffer of workgroups * 256 elements (receives checksums).  Asynchronous on stream.
+ */
+int veda_mfma_peak(float* out, int32_t iters, int32_t workgroups, void* stream);
+
+/*
  * safetensors reader (host only) for predictor files: the competition's selector
  * file holds float16 query/key projections per layer (Affine launch article, "How
  * the SN120 Competition Works"); the R2VA predictor is stored in FP8 and turned into

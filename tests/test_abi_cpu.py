@@ -237,3 +237,11 @@ def test_block_mass_and_recall_checks_before_device_calls():
     assert lib.veda_block_recall(ctypes.byref(L), None, fake, fake, None) == -1
     assert lib.veda_block_recall(ctypes.byref(L), fake, odd, fake, None) == -1
     assert lib.veda_block_recall(ctypes.byref(_layer(d=96)), fake, fake, fake, None) == -2
+
+
+def test_mfma_peak_argument_checks():
+    lib = Bnd._load()
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.veda_mfma_peak(None, 10, 4, None) == -1
+    assert lib.veda_mfma_peak(fake, 0, 4, None) == -1
+    assert lib.veda_mfma_peak(fake, 10, 0, None) == -1
