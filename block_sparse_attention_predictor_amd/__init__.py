@@ -20,6 +20,8 @@ def __getattr__(name):
         from . import binding
         return getattr(binding, name)
     if name == "build":
-        from . import build as _b
-        return _b.build
+        # importlib, not "from . import build": that form looks the name up on this
+        # package first and would re-enter this function
+        import importlib
+        return importlib.import_module(__name__ + ".build").build
     raise AttributeError(name)

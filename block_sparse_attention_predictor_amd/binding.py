@@ -133,6 +133,10 @@ def exported_symbols():
                         "veda_st_metadata_at", "veda_mfma_peak")]
 
 
+# VEDA_ABI_VERSION of include/veda.h that this binding marshals for
+ABI_VERSION = 2
+
+
 def abi_version() -> int:
     return _load().veda_abi_version()
 

@@ -37,7 +37,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert Bnd.abi_version() == 2
+    assert Bnd.abi_version() == 2 == Bnd.ABI_VERSION
     for code in range(-8, 1):
         assert Bnd.status_string(code) and "unknown" not in Bnd.status_string(code)
     assert "unknown" in Bnd.status_string(-99)
@@ -245,3 +245,11 @@ def test_mfma_peak_argument_checks():
     assert lib.veda_mfma_peak(None, 10, 4, None) == -1
     assert lib.veda_mfma_peak(fake, 0, 4, None) == -1
     assert lib.veda_mfma_peak(fake, 10, 0, None) == -1
+
+
+def test_package_entry_points_resolve():
+    """The package's lazy attributes (build included) resolve without importing in a loop."""
+    import block_sparse_attention_predictor_amd as pkg
+    import __graft_entry__ as entry
+    assert callable(pkg.build) and callable(entry.build) and callable(entry.smoke)
+    assert pkg.VedaError is Bnd.VedaError
