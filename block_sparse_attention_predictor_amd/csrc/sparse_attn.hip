@@ -5,15 +5,18 @@
 // first paragraph: the selected reference and video tiles are attended per
 // query tile and head, while text, VLM conditioning and audio stay dense.
 //
-// One workgroup computes one (b, h, query tile); each of its tile/32 waves owns
-// 32 query rows.  Keys stream through LDS in blocks of 64 tokens: first the
-// tiles named by the index row (gathered by id), then every dense range, cut
-// into 64-token blocks.
+// One workgroup computes one (b, h, query tile).  Keys stream through LDS in blocks
+// of 64 tokens: first the tiles named by the index row (gathered by id), then every
+// dense range, cut into 64-token blocks.  Two kernels share the math below:
+//  * sparse_attn_pingpong_kernel (128-row tiles): two groups of four waves split the
+//    key blocks and alternate products and softmax slot by slot (see its comment);
+//  * sparse_attn_kernel (64-row tiles, and rows whose block list exceeds the
+//    two-group kernel's LDS table): tile/32 waves, one pipeline.
 //
 // Memory path (gfx950):
 //  * K and V rows go HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per
-//    lane, no VGPR staging) into a two-stage ring; block n+1 is in flight while
-//    block n is multiplied, with one workgroup barrier per block.
+//    lane, no VGPR staging) into two-stage rings; the next blocks are in flight while
+//    the current one is multiplied.
 //  * Rows are stored unpadded with their 16-byte chunks XOR-swizzled by row, so
 //    the matrix-core operand reads below are free of LDS bank conflicts.
 //  * V stays row-major; the transposing LDS read (ds_read_b64_tr_b16) hands each
@@ -399,6 +402,518 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   }
 }
 
+// Block table of one (b, h, query tile) for the ping-pong kernel: the key blocks in the
+// order BlockIter yields them, as (first token, rows), built once per workgroup by one
+// wave with vector loads and lane ballots (tiles hold at most two 64-key blocks), so
+// that the main loop reads one LDS entry per block instead of walking the index row.
+constexpr int kTabCap = 3072;
+
+__device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseDev& DN,
+                                                 const int32_t* idx_row, int lane, int2* tab) {
+  int count = 0;
+  const int bpt = L.tile / KB;   // 1 or 2
+  for (int s = 0; s < L.n_seg; ++s) {
+    const int koff = L.seg[s].koff, K = L.seg[s].K;
+    const int64_t len = L.seg[s].len, start = L.seg[s].start;
+    for (int c0 = 0; c0 < K; c0 += 64) {
+      const int e = c0 + lane;
+      const bool in = e < K;
+      const int t = in ? (idx_row ? idx_row[koff + e] : e) : 0;
+      // the first -1 ends this segment's block
+      const uint64_t negm = __builtin_amdgcn_ballot_w64(in && t < 0);
+      const int limit = negm ? (int)__builtin_ctzll(negm) : 64;
+      int nb = 0;
+      int64_t rem = 0;
+      if (in && lane < limit) {
+        rem = len - (int64_t)t * L.tile;
+        nb = rem <= 0 ? 0 : (rem >= (int64_t)bpt * KB ? bpt : (int)((rem + KB - 1) / KB));
+      }
+      const uint64_t b1 = __builtin_amdgcn_ballot_w64(nb == 1);
+      const uint64_t b2 = __builtin_amdgcn_ballot_w64(nb == 2);
+      const int pre = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0)) +
+                      2 * (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0));
+      for (int sb = 0; sb < nb; ++sb) {
+        const int64_t r2 = rem - (int64_t)sb * KB;
+        const int pos = count + pre + sb;
+        if (pos < kTabCap)
+          tab[pos] = make_int2((int)(start + (int64_t)t * L.tile + (int64_t)sb * KB), (int)(r2 < KB ? r2 : KB));
+      }
+      count += __builtin_popcountll(b1) + 2 * __builtin_popcountll(b2);
+      if (negm) break;
+    }
+  }
+  for (int r = 0; r < DN.n; ++r) {
+    const int64_t len = DN.r[r].len, st = DN.r[r].start;
+    const int nbr = (int)((len + KB - 1) / KB);
+    for (int b0 = 0; b0 < nbr; b0 += 64) {
+      const int bi = b0 + lane;
+      const int pos = count + bi;
+      if (bi < nbr && pos < kTabCap) {
+        const int64_t r2 = len - (int64_t)bi * KB;
+        tab[pos] = make_int2((int)(st + (int64_t)bi * KB), (int)(r2 < KB ? r2 : KB));
+      }
+    }
+    count += nbr;
+  }
+  return count;
+}
+
+// Two-group ("ping-pong") form for 128-row tiles.  Eight waves in two groups of four
+// work on the same 128 query rows: group 0 takes the even key blocks of the row's block
+// list, group 1 the odd ones, each with its own two-stage K and V rings.  Workgroup
+// barriers cut time into slots; in every slot one group runs its products (PV of its
+// previous block, then S^T of its current block: MFMAs and LDS reads only) while the
+// other runs the softmax of its current block, so the two waves sharing a SIMD keep the
+// matrix core and the vector ALU busy at once.  Group 1 runs one slot behind group 0.
+// DMA: a group's K tile is loaded by its own softmax slot, its V tile by the other
+// group's products slot after the last product (where that wave would otherwise wait at
+// the barrier); every wave ends each slot by waiting for the loads it issued two slots
+// earlier.  The two partial results (each with its own running maximum) are merged
+// through LDS at the end.
+template <int D>
+__global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
+    LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int NW = 4;                       // waves per group
+  constexpr int NT = 64 * NW;                 // threads per group
+  constexpr int CPR = D / 8;
+  constexpr int SLOTS = KB * CPR;
+  constexpr int LPT = SLOTS / NT;             // DMA loads per thread per tensor and block
+  constexpr int NPV = (D / 32) * 4;           // PV products per block
+  constexpr int NS = D / 8;                   // S^T products per block
+  static_assert(SLOTS % NT == 0 && 2 * LPT < 16, "block split");
+
+  // one array per group: K stage 0, K stage 1, V stage 0, V stage 1 (the DMA is issued
+  // from inline assembly, so no compiler-inserted wait depends on their aliasing)
+  __shared__ __attribute__((aligned(1024))) uint16_t sg0[4 * KB * D], sg1[4 * KB * D];
+  __shared__ float2 sml[NW * 64];
+  __shared__ int2 stab[kTabCap];
+  __shared__ int snblk;
+
+  const int tid = threadIdx.x;
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int per_xcd = (L.Tq + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int bh = slot / per_xcd;
+  const int qt = xcd * per_xcd + (slot - bh * per_xcd);
+  if (qt >= L.Tq) return;
+  const int h = bh % L.H;
+  const int b = bh / L.H;
+
+  const int64_t q_first = L.q0 + (int64_t)qt * L.tile;
+  const int64_t q_end = L.q0 + L.qlen;
+  const int64_t head_off = (int64_t)b * L.sb + (int64_t)h * L.sh;
+  const int32_t* const idx_row = idx ? idx + ((int64_t)bh * L.Tq + qt) * L.Ktot : nullptr;
+
+  const int64_t my_q = q_first + wave * 32 + l32;
+  const bool q_ok = my_q < q_end;
+  bf16x8 qv[D / 16];
+  {
+    const uint16_t* qp = q + head_off + (q_ok ? my_q : q_first) * L.sn + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      uint4 w = q_ok ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      qv[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q is in registers before any DMA is issued
+  }
+
+  if (tid < 64) {
+    const int n = build_block_table(L, DN, idx_row, lane, stab);
+    if (lane == 0) snblk = n;
+  }
+  __syncthreads();
+  const int nblk = __builtin_amdgcn_readfirstlane(snblk);
+
+  auto dma_row = [&](int i) { return ((wave * LPT + i) * 64 + lane) / CPR; };
+  auto dma_col = [&](int i, bool is_v) {
+    const int r = dma_row(i);
+    const int pc = ((wave * LPT + i) * 64 + lane) % CPR;
+    return (pc ^ (is_v ? swz_v<CPR>(r) : swz_k<CPR>(r))) * 8;
+  };
+  uint32_t koff[LPT], voff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    koff[i] = (uint32_t)(((int64_t)dma_row(i) * L.sn + dma_col(i, false)) * 2);
+    voff[i] = (uint32_t)(((int64_t)dma_row(i) * L.sn + dma_col(i, true)) * 2);
+  }
+  const char* kbase = reinterpret_cast<const char*>(k + head_off);
+  const char* vbase = reinterpret_cast<const char*>(v + head_off);
+  // One 16-byte-per-lane HBM -> LDS load.  Issued from inline assembly so that the
+  // compiler's wait-count pass does not see it: it would otherwise wait for every LDS
+  // DMA in flight before each LDS operand read.  All waits for these loads are explicit
+  // (s_waitcnt vmcnt) and ordered by the workgroup barriers.
+  auto dma1 = [](const char* g, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_addr), "v"(off), "s"(g)
+                 : "memory", "m0");
+  };
+  auto dma = [&](const char* base, const uint32_t* off, const Block& blk, uint16_t* dst) {
+    const char* g = base + blk.start * L.sn * 2;
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t)(reinterpret_cast<char*>(dst) + wave * LPT * 1024);
+    if (blk.n == KB) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        uint32_t o = off[i];
+        asm volatile("" : "+v"(o));
+        dma1(g, o, l0 + i * 1024);
+      }
+    } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln) : : "memory");
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int r = ((wave * LPT + i) * 64 + ln) / CPR;
+        const int rc = r < blk.n ? r : blk.n - 1;
+        dma1(g, off[i] - (uint32_t)((r - rc) * (int)L.sn * 2), l0 + i * 1024);
+      }
+    }
+  };
+  // workgroup barrier without a memory fence (outstanding DMA is waited for explicitly)
+  auto barrier = []() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" : : : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // wait until at most n of this wave's DMA loads are outstanding (n in {0, LPT, 2 LPT})
+  auto wait_vm = [](int n) {
+    if (n == 2 * LPT) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPT));
+    else if (n == LPT) __builtin_amdgcn_s_waitcnt(0x0F70 | LPT);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int vg2 = (lane >> 4) & 1;
+  const int vj = lane & 15;
+  const uint32_t kR = (uint32_t)l32 * (D * 2) + ((uint32_t)(hi ^ swz_k<CPR>(l32)) << 4);
+  const int vrow0 = 4 * hi + (vj >> 2);
+  const int vdcol0 = 16 * vg2 + 4 * (vj & 3);
+  const uint32_t vR = (uint32_t)vrow0 * (D * 2) +
+                      ((uint32_t)((vdcol0 >> 3) ^ swz_v<CPR>(vrow0)) << 4) + (uint32_t)(vdcol0 & 7) * 2;
+
+  auto body = [&](auto G) {
+    constexpr int GRP = decltype(G)::value;
+    int j = 0;
+    uint16_t* const Gb = GRP ? sg1 : sg0;
+    uint16_t* const Ks0 = Gb;
+    uint16_t* const Ks1 = Gb + KB * D;
+    uint16_t* const Vs0 = Gb + 2 * KB * D;
+    uint16_t* const Vs1 = Gb + 3 * KB * D;
+    // operand addresses: group base plus the lane's swizzled offset for every K column
+    // step and every V column block; stage and row offsets are instruction immediates
+    const uint32_t gbase = (uint32_t)(uintptr_t)(lds_void_t)Gb;
+    uint32_t kA[D / 16], vA[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kA[kk] = gbase + (kR ^ (kk << 5));
+      asm volatile("" : "+v"(kA[kk]));
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      vA[db] = gbase + (vR ^ (db << 6));
+      asm volatile("" : "+v"(vA[db]));
+    }
+    // A products slot with no previous block multiplies P = 0 by a V stage: both stages
+    // start zeroed so that a stage no DMA has filled yet holds finite values.
+    {
+      uint4* z = reinterpret_cast<uint4*>(Vs0);
+#pragma unroll
+      for (int i = 0; i < 2 * KB * D * 2 / 16 / NT; ++i) z[i * NT + (tid & (NT - 1))] = make_uint4(0, 0, 0, 0);
+    }
+
+    // this group's j-th block c_j is block 2j + GRP of the table; K(c_j) and V(c_j)
+    // live in stage j % 2
+    auto entry = [&](int i) {
+      if (i >= nblk) return Block{0, 0};
+      const int2 e = stab[i];
+      return Block{(int64_t)__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y)};
+    };
+    Block cur = entry(GRP);                   // c_j
+    Block nx1 = entry(2 + GRP);               // c_{j+1}
+    Block nx2 = entry(4 + GRP);               // c_{j+2}
+    Block prev{0, 0};                         // c_{j-1}
+    if (cur.n > 0) dma(kbase, koff, cur, Ks0);
+    if (nx1.n > 0) dma(kbase, koff, nx1, Ks1);
+    int np = 0;                               // this wave's loads issued in the previous phase
+    if (cur.n > 0) {
+      dma(vbase, voff, cur, Vs0);
+      np = LPT;
+    }
+    wait_vm(np);                              // K(c_0) and K(c_1) landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the zeroed V stages are written
+    barrier();
+    if (GRP) {                                // group 1 runs one slot behind
+      barrier();
+      np = 0;
+    }
+    // V tile the products slot issues for the other group: group 1's slot j loads group 0's
+    // block j + 1, group 0's slot j (j >= 1) loads group 1's block j
+    Block xo = GRP ? entry(2) : Block{0, 0};
+    uint16_t* const Go = GRP ? sg0 : sg1;
+
+    f32x16 s[2];
+    bf16x8 pb[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)0.f;
+
+    typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8_t;
+    auto read_v = [&](int ST, bf16x8 (&va)[D / 32][4]) {   // V stage ST
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          s16x4 part[2];
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t)(uintptr_t)(vA[db] + (2 + ST) * KB * D * 2 + (16 * c + 8 * r) * D * 2));
+          const s16x8 both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          va[db][c] = __builtin_bit_cast(bf16x8, both);
+        }
+    };
+    auto read_k = [&](int ST, bf16x8 (&ka)[2][D / 16]) {   // K stage ST
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          ka[mb][kk] = *(lds_bf16x8_t)(uintptr_t)(kA[kk] + ST * KB * D * 2 + mb * 32 * D * 2);
+    };
+    auto mul_pv = [&](const bf16x8 (&va)[D / 32][4]) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[c], o[db], 0, 0, 0);
+    };
+    auto mul_s = [&](const bf16x8 (&ka)[2][D / 16]) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mb][kk], qv[kk], s[mb], 0, 0, 0);
+    };
+
+    // products slot of c_j: PV of c_{j-1} (V stage (j-1)%2), S^T of c_j (K stage j%2).
+    // Always both, with no branch: a missing c_{j-1} has P = 0 against finite V stage
+    // contents (adds exactly zero), a missing c_j gives S^T values that nothing reads.
+    // Operand reads run four products ahead; no VALU instruction is left in this slot.
+    auto mphase = [&](auto stage) {
+      constexpr int ST = decltype(stage)::value;
+      bf16x8 va[D / 32][4];
+      bf16x8 ka[2][D / 16];
+      read_v(1 - ST, va);
+      read_k(ST, ka);
+      mul_pv(va);
+      mul_s(ka);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < NPV - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      int nc = 0;
+      if (xo.n > 0) {
+        // group 1 fills group 0's V stage (j+1)%2, group 0 fills group 1's V stage j%2
+        dma(vbase, voff, xo, Go + (2 + (GRP ? 1 - ST : ST)) * KB * D);
+        nc = LPT;
+      }
+      wait_vm(nc + np);                       // loads of two phases ago have landed
+      np = nc;
+      barrier();
+    };
+    // softmax slot of c_j.  First the DMA of K(c_{j+2}) into the K stage the products slot
+    // has just released (j%2), then the softmax; the table entries of c_{j+3} and of the
+    // other group's next V tile are read here for the following slots.
+    auto vphase = [&](auto stage) {
+      constexpr int ST = decltype(stage)::value;
+      uint16_t* Kf = ST ? Ks1 : Ks0;
+      const int i3 = 2 * (j + 3) + GRP;
+      const int2 e3 = i3 < nblk ? stab[i3] : make_int2(0, 0);
+      const int io = GRP ? 2 * (j + 2) : 2 * (j + 1) + 1;
+      const int2 eo = io < nblk ? stab[io] : make_int2(0, 0);
+      int nc = 0;
+      if (nx2.n > 0) {
+        dma(kbase, koff, nx2, Kf);
+        nc = LPT;
+      }
+      if (cur.n > 0) {
+        const int n = cur.n;
+        if (n < KB) {
+          int kb = hi * 4;
+          float ninf = -INFINITY;
+          asm volatile("" : "+v"(kb), "+v"(ninf) : : "memory");
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int c = mb * 32 + (e >> 2) * 8 + (e & 3);
+              if (kb >= n - c) s[mb][e] = ninf;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+        }
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
+          const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, l_run, false);
+        }
+      } else {
+        // no block: the next PV adds zero
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)0.f;
+      }
+      const Block nx3{(int64_t)__builtin_amdgcn_readfirstlane(e3.x), __builtin_amdgcn_readfirstlane(e3.y)};
+      xo = Block{(int64_t)__builtin_amdgcn_readfirstlane(eo.x), __builtin_amdgcn_readfirstlane(eo.y)};
+      wait_vm(nc + np);                       // loads of two phases ago have landed
+      np = nc;
+      __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): no scalar load stays in flight
+      barrier();
+      prev = cur;
+      cur = nx1;
+      nx1 = nx2;
+      nx2 = nx3;
+      ++j;
+    };
+    // slots: ceil(nblk / 2) + 1 products/softmax pairs, the same count in both groups
+    const int iters = nblk > 0 ? (nblk + 1) / 2 + 1 : 0;
+    while (j < iters) {
+      mphase(std::integral_constant<int, 0>{});
+      vphase(std::integral_constant<int, 0>{});
+      if (j >= iters) break;
+      mphase(std::integral_constant<int, 1>{});
+      vphase(std::integral_constant<int, 1>{});
+    }
+    if (!GRP) barrier();                      // group 0 matches group 1's first slot
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): no DMA left in flight
+  };
+  if (grp == 0)
+    body(std::integral_constant<int, 0>{});
+  else
+    body(std::integral_constant<int, 1>{});
+
+  // ---- merge group 1's partial result into group 0's (K/V stages are free now)
+  __syncthreads();
+  float4* const mo = reinterpret_cast<float4*>(sg0) + wave * 16 * 64 + lane;
+  if (grp) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        mo[(db * 4 + e4) * 64] = make_float4(o[db][4 * e4], o[db][4 * e4 + 1], o[db][4 * e4 + 2], o[db][4 * e4 + 3]);
+    sml[wave * 64 + lane] = make_float2(m_run, l_run);
+  }
+  __syncthreads();
+  if (grp) return;
+  {
+    const float2 ml = sml[wave * 64 + lane];
+    const float m = fmaxf(m_run, ml.x);
+    const float fa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float fb = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const float4 w = mo[(db * 4 + e4) * 64];
+        o[db][4 * e4 + 0] = o[db][4 * e4 + 0] * fa + w.x * fb;
+        o[db][4 * e4 + 1] = o[db][4 * e4 + 1] * fa + w.y * fb;
+        o[db][4 * e4 + 2] = o[db][4 * e4 + 2] * fa + w.z * fb;
+        o[db][4 * e4 + 3] = o[db][4 * e4 + 3] * fa + w.w * fb;
+      }
+    l_run = l_run * fa + ml.y * fb;
+    m_run = m;
+  }
+
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (q_ok) {
+    uint16_t* op = out + head_off + my_q * L.sn;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + i * 8 + hi * 4;
+        const __bf16 o0 = (__bf16)(o[db][i * 4 + 0] * inv);
+        const __bf16 o1 = (__bf16)(o[db][i * 4 + 1] * inv);
+        const __bf16 o2 = (__bf16)(o[db][i * 4 + 2] * inv);
+        const __bf16 o3 = (__bf16)(o[db][i * 4 + 3] * inv);
+        uint2 w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, o2) | ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
+        *reinterpret_cast<uint2*>(op + d0) = w;
+      }
+    if (lse && hi == 0) {
+      lse[(int64_t)bh * L.qlen + (my_q - L.q0)] =
+          (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void* q, const void* k,
@@ -413,7 +928,24 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void*
   auto kk = static_cast<const uint16_t*>(k);
   auto vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(out);
-  if (L.d == 128 && L.tile == 128)
+  // 128-row tiles take the two-group kernel when the row's block list fits its LDS table
+  // and every token index fits the table's 32-bit entries
+  int64_t bound = (int64_t)L.Ktot * (L.tile / KB);
+  int64_t last = 0;
+  for (int i = 0; i < DN.n; ++i) {
+    bound += (DN.r[i].len + KB - 1) / KB;
+    last = DN.r[i].start + DN.r[i].len > last ? DN.r[i].start + DN.r[i].len : last;
+  }
+  for (int i = 0; i < L.n_seg; ++i)
+    last = L.seg[i].start + L.seg[i].len > last ? L.seg[i].start + L.seg[i].len : last;
+  const bool two_group = L.tile == 128 && bound <= kTabCap && last < ((int64_t)1 << 31);
+  if (two_group && L.d == 128)
+    hipLaunchKernelGGL((sparse_attn_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
+                       scale_log2, oo, lse);
+  else if (two_group)
+    hipLaunchKernelGGL((sparse_attn_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
+                       scale_log2, oo, lse);
+  else if (L.d == 128 && L.tile == 128)
     hipLaunchKernelGGL((sparse_attn_kernel<128, 4>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse);
   else if (L.d == 128 && L.tile == 64)
