@@ -494,6 +494,16 @@ def cpu_baseline(lay, log, budget_s=20.0):
     }
 
 
+def attention_kernel_name(wl):
+    """The attention kernel the library launches for this layer: the two-group kernel for
+    128-row tiles whose key-block list fits its 3072-entry LDS table, else the single-pipeline one."""
+    blocks = sum(min(s.budget, -(-s.length // wl.tile)) for s in wl.segments) * (wl.tile // 64)
+    blocks += sum(-(-r.length // 64) for r in wl.dense)
+    if wl.tile == 128 and blocks <= 3072:
+        return f"sparse_attn_pingpong_kernel<{wl.d}>"
+    return f"sparse_attn_kernel<{wl.d}, {wl.tile // 32}>"
+
+
 def recorded_traffic(workload):
     """HBM-side bytes per attention launch from the committed rocprofv3 byte-counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain 1 GiB copy), or None when no summary
@@ -559,6 +569,7 @@ def main():
         cpu = cpu_baseline(lay, log)
     achieved = res["actual_tflops_attn"]
     traffic = recorded_traffic(args.workload)
+    attn_kernel = attention_kernel_name(wl)
     line = {
         "metric": METRIC,
         "value": round(res["dense_equiv_tflops_step"], 3),
@@ -602,7 +613,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": (round(traffic / 1e9, 2) if traffic else None),
                      "traffic_unit": "GB per launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-                     "kernel": "sparse_attn_kernel", "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
+                     "kernel": attn_kernel, "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
         "cpu_baseline": cpu,
         "patterns": patterns,
         "also": also,
