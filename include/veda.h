@@ -173,6 +173,10 @@ int veda_select(const veda_layer* layer, const void* q, const void* k,
  *   out        : bf16 with the same strides as q.
  *   lse_opt    : NULL, or fp32 [B, H, query.len] receiving the natural-log
  *                log-sum-exp of each row's scaled logits.
+ * q, k and v must hold finite values: a non-finite K or V value read by one query
+ * tile's workgroup may make every row of that (b, h, query tile) non-finite, not only
+ * the rows whose keys include it (key blocks are multiplied with zero weights where
+ * a block is partial or missing).
  */
 int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
                      const int32_t* idx, const veda_range* dense, int32_t n_dense,
