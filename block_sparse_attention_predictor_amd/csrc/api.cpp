@@ -290,9 +290,23 @@ int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const
   if (st != VEDA_OK) return st;
   st = veda_sparse_attn(layer, q, k, v, idx, dense, n_dense, scale, out, nullptr, stream);
   if (st != VEDA_OK) return st;
-  for (int i = 0; i < n_dense_queries; ++i) {
-    if (dense_queries[i].len == 0) continue;
-    full.query = dense_queries[i];
+  // dense query ranges that touch each other run as one launch (every row attends to the
+  // same keys, so grouping rows into tiles across a boundary changes nothing)
+  veda_range merged[VEDA_MAX_DENSE];
+  int n_merged = 0;
+  for (int i = 0; i < n_dense_queries; ++i)
+    if (dense_queries[i].len > 0) merged[n_merged++] = dense_queries[i];
+  std::sort(merged, merged + n_merged,
+            [](const veda_range& a, const veda_range& b) { return a.start < b.start; });
+  int n_runs = 0;
+  for (int i = 0; i < n_merged; ++i) {
+    if (n_runs > 0 && merged[n_runs - 1].start + merged[n_runs - 1].len == merged[i].start)
+      merged[n_runs - 1].len += merged[i].len;
+    else
+      merged[n_runs++] = merged[i];
+  }
+  for (int i = 0; i < n_runs; ++i) {
+    full.query = merged[i];
     st = veda_sparse_attn(&full, q, k, v, nullptr, dense, n_dense, scale, out, nullptr, stream);
     if (st != VEDA_OK) return st;
   }

@@ -114,11 +114,35 @@ __device__ __forceinline__ int swz_k(int row) { return row & (CPR - 1); }
 template <int CPR>
 __device__ __forceinline__ int swz_v(int row) { return (row & 3) * (CPR / 4); }
 
+// Work item of a workgroup, XCD-aware: workgroups are dispatched round-robin over the
+// 8 XCDs (blockIdx % 8).
+//  * by tiles (index rows given): every XCD works on the same (b, h) at a time and takes
+//    a contiguous slice of its query tiles.  The head's K/V (tens of MB) then stays in the
+//    shared Infinity Cache while it is in use, and neighbouring query tiles, whose
+//    selections overlap, share each XCD's L2.
+//  * by heads (no index: every tile of every segment, e.g. the dense query rows of a
+//    layer): every XCD takes whole heads, so the query tiles of one head, which read the
+//    same keys in the same order, run side by side and share that XCD's L2.
+// Returns false for a padding workgroup (a uniform exit before any barrier).
+__device__ __forceinline__ bool work_item(const LayerDev& L, int by_heads, int& bh, int& qt) {
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  if (by_heads) {
+    bh = (slot / L.Tq) * 8 + xcd;
+    qt = slot % L.Tq;
+    return bh < L.B * L.H;
+  }
+  const int per_xcd = (L.Tq + 7) >> 3;            // query tiles per XCD and head
+  bh = slot / per_xcd;
+  qt = xcd * per_xcd + (slot - bh * per_xcd);
+  return qt < L.Tq;
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
   constexpr int NT = 64 * NW;                 // threads
   constexpr int CPR = D / 8;                  // 16-byte chunks per key row
   constexpr int SLOTS = KB * CPR;             // 16-byte slots per K (or V) block
@@ -138,17 +162,8 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item, XCD-aware.  Workgroups are dispatched round-robin over the 8
-  // XCDs (blockIdx % 8).  Every XCD works on the same (b, h) at a time and takes a
-  // contiguous slice of its query tiles: the head's K/V (tens of MB) then stays in
-  // the shared Infinity Cache while it is in use, and neighbouring query tiles,
-  // whose selections overlap, share each XCD's L2.
-  const int per_xcd = (L.Tq + 7) >> 3;           // query tiles per XCD and head
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int bh = slot / per_xcd;
-  const int qt = xcd * per_xcd + (slot - bh * per_xcd);
-  if (qt >= L.Tq) return;                          // padding workgroup (uniform exit)
+  int bh, qt;
+  if (!work_item(L, by_heads, bh, qt)) return;     // padding workgroup (uniform exit)
   const int h = bh % L.H;
   const int b = bh / L.H;
 
@@ -474,7 +489,7 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
   constexpr int NW = 4;                       // waves per group
   constexpr int NT = 64 * NW;                 // threads per group
   constexpr int CPR = D / 8;
@@ -498,12 +513,8 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int per_xcd = (L.Tq + 7) >> 3;
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int bh = slot / per_xcd;
-  const int qt = xcd * per_xcd + (slot - bh * per_xcd);
-  if (qt >= L.Tq) return;
+  int bh, qt;
+  if (!work_item(L, by_heads, bh, qt)) return;     // padding workgroup (uniform exit)
   const int h = bh % L.H;
   const int b = bh / L.H;
 
@@ -919,8 +930,9 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void* q, const void* k,
                               const void* v, const int32_t* idx, float scale, void* out, float* lse,
                               hipStream_t s) {
+  const int by_heads = idx == nullptr && L.B * L.H >= 8;
   const int64_t per_xcd = (L.Tq + 7) / 8;
-  const int64_t nwork = (int64_t)L.B * L.H * per_xcd * 8;
+  const int64_t nwork = by_heads ? ((int64_t)L.B * L.H + 7) / 8 * 8 * L.Tq : (int64_t)L.B * L.H * per_xcd * 8;
   if (nwork > 0x7FFFFFFF) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
   dim3 grid((unsigned)nwork);
@@ -941,22 +953,22 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void*
   const bool two_group = L.tile == 128 && bound <= kTabCap && last < ((int64_t)1 << 31);
   if (two_group && L.d == 128)
     hipLaunchKernelGGL((sparse_attn_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse);
+                       scale_log2, oo, lse, by_heads);
   else if (two_group)
     hipLaunchKernelGGL((sparse_attn_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse);
+                       scale_log2, oo, lse, by_heads);
   else if (L.d == 128 && L.tile == 128)
     hipLaunchKernelGGL((sparse_attn_kernel<128, 4>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse);
+                       scale_log2, oo, lse, by_heads);
   else if (L.d == 128 && L.tile == 64)
     hipLaunchKernelGGL((sparse_attn_kernel<128, 2>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse);
+                       scale_log2, oo, lse, by_heads);
   else if (L.d == 64 && L.tile == 128)
     hipLaunchKernelGGL((sparse_attn_kernel<64, 4>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse);
+                       scale_log2, oo, lse, by_heads);
   else
     hipLaunchKernelGGL((sparse_attn_kernel<64, 2>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse);
+                       scale_log2, oo, lse, by_heads);
   return hipGetLastError();
 }
 

@@ -59,8 +59,13 @@ def test_layer_attn_matches_oracle(d, tile):
                 check_attn(o[b, st:st + ln, h], ref)
 
 
-def test_no_index_equals_every_tile():
-    L, q, k, v, wq, wk, segments, dense, dq = _case(7)
+@pytest.mark.parametrize("H,tile", [(3, 64), (8, 64), (8, 128)])
+def test_no_index_equals_every_tile(H, tile):
+    """No index = an index row listing every tile.  With 8 or more (b, h) pairs the no-index
+    launch maps whole heads to XCDs instead of slicing each head's tiles over them; the
+    mapping changes which workgroup computes an item, not the arithmetic, so the outputs
+    are bit-identical."""
+    L, q, k, v, wq, wk, segments, dense, dq = _case(7, tile=tile, H=H)
     full = [(st, ln, 10 ** 6) for (st, ln, _) in segments]
     Lf = Bnd.make_layer(B=1, H=L.H, d=L.d, p=L.p, tile=L.tile, n_tokens=L.n_tokens, query=(0, 640),
                         segments=full, strides=(L.stride_b, L.stride_n, L.stride_h))
@@ -109,3 +114,24 @@ def test_all_padding_without_dense_gives_zero_rows():
     o = bf16_to_f64(out)
     assert np.all(o[0, 4 * L.tile:5 * L.tile, 1] == 0.0)
     assert np.all(np.isfinite(o[0, :640]))
+
+
+def test_layer_attn_heads_mapping_and_adjacent_dense_query_ranges():
+    """B x H = 8: the dense query rows run with whole heads per XCD; the three touching
+    dense query ranges (reference, text, audio) run as one launch, in whatever order the
+    caller lists them.  Against the oracle, and bit-identical across orders."""
+    L, q, k, v, wq, wk, segments, dense, dq = _case(11, d=128, tile=128, H=4, B=2)
+    qd, kd, vd, wqd, wkd = (to_dev_bf16(x) for x in (q, k, v, wq, wk))
+    out, idx = Bnd.layer_attn(L, qd, kd, vd, wqd, wkd, dense, dq)
+    out_r, idx_r = Bnd.layer_attn(L, qd, kd, vd, wqd, wkd, dense, list(reversed(dq)))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_r) and torch.equal(idx, idx_r)
+    o = bf16_to_f64(out)
+    res = O.attend(q, k, v, idx.cpu().numpy(), L.tile, (0, 640), segments, dense)
+    got = np.concatenate([o[b, t * L.tile:min((t + 1) * L.tile, 640), h] for (b, h, t) in res])
+    check_attn(got, np.concatenate([r[0] for r in res.values()]))
+    st, ln = dq[0][0], sum(n for _, n in dq)          # one merged run of rows
+    for b in range(L.B):
+        for h in range(L.H):
+            ref, _ = O.attend_all_keys(q, k, v, b, h, (st, ln), segments, dense)
+            check_attn(o[b, st:st + ln, h], ref)
