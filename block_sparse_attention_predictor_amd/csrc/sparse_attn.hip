@@ -72,8 +72,9 @@ struct BlockIter {
   int sel = 0, sub = 0, seg = 0, dr = 0;
   int64_t doff = 0;
 
+  template <int KBK = KB>
   __device__ __forceinline__ Block next(const LayerDev& L, const DenseDev& DN, const_i32_t idx_row) {
-    const int bpt = L.tile / KB;
+    const int bpt = L.tile / KBK;
     for (;;) {
       if (sel < L.Ktot) {
         while (sel >= L.seg[seg].koff + L.seg[seg].K) ++seg;
@@ -83,25 +84,25 @@ struct BlockIter {
           sub = 0;
           continue;
         }
-        const int64_t rel = (int64_t)t * L.tile + (int64_t)sub * KB;
+        const int64_t rel = (int64_t)t * L.tile + (int64_t)sub * KBK;
         const int64_t rem = L.seg[seg].len - rel;
         const int64_t st = L.seg[seg].start + rel;
         if (++sub == bpt) {
           sub = 0;
           ++sel;
         }
-        if (rem > 0) return Block{st, (int)(rem < KB ? rem : KB)};
+        if (rem > 0) return Block{st, (int)(rem < KBK ? rem : KBK)};
         continue;
       }
       if (dr < DN.n) {
         const int64_t rem = DN.r[dr].len - doff;
         const int64_t st = DN.r[dr].start + doff;
-        doff += KB;
+        doff += KBK;
         if (doff >= DN.r[dr].len) {
           ++dr;
           doff = 0;
         }
-        return Block{st, (int)(rem < KB ? rem : KB)};
+        return Block{st, (int)(rem < KBK ? rem : KBK)};
       }
       return Block{0, 0};
     }
@@ -138,23 +139,25 @@ __device__ __forceinline__ bool work_item(const LayerDev& L, int by_heads, int& 
   return qt < L.Tq;
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
+template <int D, int NW, int KBK>
+__global__ __launch_bounds__(64 * NW, KBK == 32 ? 4 : 2) void sparse_attn_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
   constexpr int NT = 64 * NW;                 // threads
   constexpr int CPR = D / 8;                  // 16-byte chunks per key row
-  constexpr int SLOTS = KB * CPR;             // 16-byte slots per K (or V) block
+  constexpr int SLOTS = KBK * CPR;            // 16-byte slots per K (or V) block
   constexpr int LPT = SLOTS / NT;             // DMA loads per thread per tensor and block
-  static_assert(SLOTS % NT == 0, "block split");
+  constexpr int MBN = KBK / 32;               // 32-key halves of S^T per block
+  constexpr int PCN = KBK / 16;               // 16-key slices of the PV contraction
+  static_assert(SLOTS % NT == 0 && (KBK == 32 || KBK == 64), "block split");
 
   // two stages each for K and V
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * KB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * KBK * D];
   uint16_t* const Ks0 = smem;
-  uint16_t* const Ks1 = smem + KB * D;
-  uint16_t* const Vs0 = smem + 2 * KB * D;
-  uint16_t* const Vs1 = smem + 3 * KB * D;
+  uint16_t* const Ks1 = smem + KBK * D;
+  uint16_t* const Vs0 = smem + 2 * KBK * D;
+  uint16_t* const Vs1 = smem + 3 * KBK * D;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   auto dma = [&](const char* base, const uint32_t* off, bool is_v, const Block& blk,
                  uint16_t* dst) {
     const char* g = base + blk.start * L.sn * 2;
-    if (blk.n == KB) {
+    if (blk.n == KBK) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         uint32_t o = off[i];
@@ -261,8 +264,8 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   //   O^T += V_i^T P_i^T
   // so every DMA has a whole iteration to land and there is one barrier per block.
   BlockIter it;
-  Block b0 = it.next(L, DN, idx_row);
-  Block b1 = it.next(L, DN, idx_row);
+  Block b0 = it.next<KBK>(L, DN, idx_row);
+  Block b1 = it.next<KBK>(L, DN, idx_row);
   if (b0.n > 0) {
     dma(kbase, koff, false, b0, Ks0);
     dma(vbase, voff, true, b0, Vs0);
@@ -277,36 +280,36 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     uint16_t* Vc = ST ? Vs1 : Vs0;
     const int n = b0.n;
 
-    // ---- S^T = K Q^T for 64 keys: two 32-key halves
-    f32x16 s[2];
-    bf16x8 ka[2][D / 16];
+    // ---- S^T = K Q^T for the block's keys, in 32-key halves
+    f32x16 s[MBN];
+    bf16x8 ka[MBN][D / 16];
     const char* Kb = reinterpret_cast<const char*>(Kc);
     uint32_t kRi = kR;   // kept in one register: the per-kk addresses are formed in the loop
     asm volatile("" : "+v"(kRi));
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MBN; ++mb)
         ka[mb][kk] = *reinterpret_cast<const bf16x8*>(Kb + (kRi ^ (kk << 5)) + mb * 32 * D * 2);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MBN; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MBN; ++mb)
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mb][kk], qv[kk], s[mb], 0, 0, 0);
     // all operand reads first, then the products (the reads' latency is paid once)
-    __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MBN * D / 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MBN * D / 16, 0);
     // ---- mask keys past the end of a partial block (tile-uniform branch)
-    if (n < KB) {
+    if (n < KBK) {
       int kb = hi * 4;                      // key = kb + c for accumulator entry (mb, e)
       float ninf = -INFINITY;
       asm volatile("" : "+v"(kb), "+v"(ninf) : : "memory");   // a real branch, not selects
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MBN; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = mb * 32 + (e >> 2) * 8 + (e & 3);
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     // ---- online softmax, exp2 domain, lazy rescale
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MBN; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
     {
@@ -333,15 +336,15 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
     }
-    bf16x8 pb[4];
+    bf16x8 pb[PCN];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MBN; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
     // row sum of the bf16 weights the second product uses (two per instruction)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < PCN; ++c) {
       const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
       const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
       l_run = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, l_run, false);
@@ -351,18 +354,18 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     }
 
     // next block two ahead (its scalar index load overlaps the barrier wait)
-    const Block b2 = it.next(L, DN, idx_row);
+    const Block b2 = it.next<KBK>(L, DN, idx_row);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA (V_i, K_{i+1}) landed
     __syncthreads();
 
     // ---- V^T operands of this block, then the next DMA, then O^T += V^T P^T
     uint32_t vRi = vR;
     asm volatile("" : "+v"(vRi));
-    bf16x8 va[D / 32][4];
+    bf16x8 va[D / 32][PCN];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < PCN; ++c) {
         s16x4 part[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < PCN; ++c)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[c], o[db], 0, 0, 0);
     b0 = b1;
     b1 = b2;
@@ -958,16 +961,16 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void*
     hipLaunchKernelGGL((sparse_attn_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
   else if (L.d == 128 && L.tile == 128)
-    hipLaunchKernelGGL((sparse_attn_kernel<128, 4>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
+    hipLaunchKernelGGL((sparse_attn_kernel<128, 4, 64>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
   else if (L.d == 128 && L.tile == 64)
-    hipLaunchKernelGGL((sparse_attn_kernel<128, 2>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
+    hipLaunchKernelGGL((sparse_attn_kernel<128, 2, 32>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
   else if (L.d == 64 && L.tile == 128)
-    hipLaunchKernelGGL((sparse_attn_kernel<64, 4>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
+    hipLaunchKernelGGL((sparse_attn_kernel<64, 4, 64>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
   else
-    hipLaunchKernelGGL((sparse_attn_kernel<64, 2>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
+    hipLaunchKernelGGL((sparse_attn_kernel<64, 2, 32>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
   return hipGetLastError();
 }
