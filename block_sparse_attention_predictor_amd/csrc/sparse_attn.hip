@@ -6,12 +6,13 @@
 // query tile and head, while text, VLM conditioning and audio stay dense.
 //
 // One workgroup computes one (b, h, query tile).  Keys stream through LDS in blocks
-// of 64 tokens: first the tiles named by the index row (gathered by id), then every
-// dense range, cut into 64-token blocks.  Two kernels share the math below:
+// of 64 tokens (32 for 64-row tiles): first the tiles named by the index row (gathered
+// by id), then every dense range, cut into blocks.  Two kernels share the math below:
 //  * sparse_attn_pingpong_kernel (128-row tiles): two groups of four waves split the
 //    key blocks and alternate products and softmax slot by slot (see its comment);
-//  * sparse_attn_kernel (64-row tiles, and rows whose block list exceeds the
-//    two-group kernel's LDS table): tile/32 waves, one pipeline.
+//  * sparse_attn_kernel (64-row tiles with 32-key blocks, which lets two workgroups'
+//    waves share each SIMD; and 128-row rows whose block list exceeds the two-group
+//    kernel's LDS table): tile/32 waves, one pipeline.
 //
 // Memory path (gfx950):
 //  * K and V rows go HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per
@@ -54,7 +55,7 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 typedef const __attribute__((address_space(4))) int32_t* const_i32_t;
 
-constexpr int KB = 64;            // keys per block
+constexpr int KB = 64;            // keys per block (the single-pipeline kernel also runs 32)
 constexpr float kLazyRescale = 8.0f;
 
 struct Block {
