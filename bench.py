@@ -523,8 +523,8 @@ def recorded_traffic(workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path is not "
-                                   "sharded across GPUs (see DESIGN.md for how it would shard)"}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the path is built and "
+                                   "measured on one GPU's share of a layer and is not sharded across GPUs"}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
