@@ -501,7 +501,7 @@ def attention_kernel_name(wl):
     blocks += sum(-(-r.length // 64) for r in wl.dense)
     if wl.tile == 128 and blocks <= 3072:
         return f"sparse_attn_pingpong_kernel<{wl.d}>"
-    return f"sparse_attn_kernel<{wl.d}, {wl.tile // 32}>"
+    return f"sparse_attn_kernel<{wl.d}, {wl.tile // 32}, {32 if wl.tile == 64 else 64}>"
 
 
 def recorded_traffic(workload):

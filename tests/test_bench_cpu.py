@@ -1,0 +1,32 @@
+"""bench.py on the host: the one-GPU contract and the kernel it names for each layer."""
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+from block_sparse_attention_predictor_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_attention_kernel_name_follows_the_launcher_rule():
+    """128-row tiles whose block list fits 3072 table entries take the two-group kernel."""
+    b = _bench()
+    names = {n: b.attention_kernel_name(wl) for n, wl in I.WORKLOADS.items()}
+    assert names["t2v5s"] == names["r2va"] == names["t2v14s"] == "sparse_attn_pingpong_kernel<128>"
+    assert names["mid"] == "sparse_attn_kernel<128, 2, 32>" and names["tiny"] == "sparse_attn_kernel<64, 2, 32>"
