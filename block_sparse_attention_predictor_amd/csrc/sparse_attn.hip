@@ -33,10 +33,13 @@
 // without a shuffle
 // (the key order inside each 16-key slice of the O^T contraction is permuted to
 // match the accumulator layout; the V^T reads use the same permutation).
-// Softmax is fp32 in the exp2 domain with a lazily updated running maximum: the
-// output is rescaled only when a block's maximum exceeds the running one by
-// more than 2^8, which leaves the result unchanged (numerator and denominator
-// share the stale maximum) and removes the per-block rescale in the common case.
+// Softmax is fp32 in the exp2 domain against a lazily updated running maximum.
+// A block's weights are first taken against the running maximum as it stands and
+// kept when no lane's sum of them exceeds 2^8 (then no single weight does); the
+// stale maximum leaves the result unchanged, since numerator and denominator share
+// it.  Otherwise (always on a row's first block, rarely after) the maximum moves
+// to the block's maximum, the output is rescaled and the weights are redone, so
+// the block maximum itself is only computed on that path.
 // P is rounded to bf16 for the second product; O accumulates in fp32 and is
 // rounded to bf16 once at the end.
 #include "common.h"
@@ -56,7 +59,7 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 typedef const __attribute__((address_space(4))) int32_t* const_i32_t;
 
 constexpr int KB = 64;            // keys per block (the single-pipeline kernel also runs 32)
-constexpr float kLazyRescale = 8.0f;
+constexpr float kLazySum = 256.0f;   // largest per-lane weight sum kept against a stale maximum
 
 struct Block {
   int64_t start;
@@ -317,17 +320,39 @@ __global__ __launch_bounds__(64 * NW, KBK == 32 ? 4 : 2) void sparse_attn_kernel
           if (kb >= n - c) s[mb][e] = ninf;
         }
     }
-    // ---- online softmax, exp2 domain, lazy rescale
-    float mx = -INFINITY;
+    // ---- online softmax, exp2 domain.  Weights against the running maximum as it
+    // stands, and this lane's sum of them (of the bf16 values the second product uses)
+    bf16x8 pb[PCN];
+    auto weights = [&]() {
 #pragma unroll
-    for (int mb = 0; mb < MBN; ++mb)
+      for (int mb = 0; mb < MBN; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    {
+        for (int e = 0; e < 16; ++e)
+          pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
+      float bs = 0.f;
+#pragma unroll
+      for (int c = 0; c < PCN; ++c) {
+        const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
+        const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
+        bs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, bs, false);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, bs, false);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, bs, false);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, bs, false);
+      }
+      return bs;
+    };
+    float bs = weights();
+    // Kept while no lane's weights sum above kLazySum (so none exceeds it);
+    // otherwise (always on the first block, where m_run = -inf gives inf or NaN) the
+    // running maximum moves to this block's maximum and the weights are redone.
+    if (__builtin_amdgcn_ballot_w64(!(bs <= kLazySum)) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < MBN; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-    }
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -336,23 +361,9 @@ __global__ __launch_bounds__(64 * NW, KBK == 32 ? 4 : 2) void sparse_attn_kernel
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      bs = weights();
     }
-    bf16x8 pb[PCN];
-#pragma unroll
-    for (int mb = 0; mb < MBN; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
-    // row sum of the bf16 weights the second product uses (two per instruction)
-#pragma unroll
-    for (int c = 0; c < PCN; ++c) {
-      const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
-      const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, l_run, false);
-    }
+    l_run += bs;
 
     // next block two ahead (its scalar index load overlaps the barrier wait)
     const Block b2 = it.next<KBK>(L, DN, idx_row);
@@ -802,16 +813,37 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
               if (kb >= n - c) s[mb][e] = ninf;
             }
         }
-        float mx = -INFINITY;
+        // weights against the running maximum as it stands, and this lane's sum of them
+        auto weights = [&]() {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-        {
+            for (int e = 0; e < 16; ++e)
+              pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
+          float bs = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
+            const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
+            bs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, bs, false);
+            bs = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, bs, false);
+            bs = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, bs, false);
+            bs = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, bs, false);
+          }
+          return bs;
+        };
+        float bs = weights();
+        // Weights are kept while no lane's 32 of them sum above kLazySum (none
+        // exceeds it then).  Otherwise (the first block: m_run = -inf gives inf or NaN)
+        // the running maximum moves to this block's maximum and the weights are redone.
+        if (__builtin_amdgcn_ballot_w64(!(bs <= kLazySum)) != 0) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
           mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-        }
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
           const float m_new = fmaxf(m_run, mx);
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
@@ -820,21 +852,9 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+          bs = weights();
         }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
-          const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, l_run, false);
-        }
+        l_run += bs;
       } else {
         // no block: the next PV adds zero
 #pragma unroll
