@@ -35,6 +35,14 @@ selection keeps:
       averaged over the rows)
   T2  recall of an index set: the selected tiles' share of the segment tiles' mass
 
+the FP8 form of O7's first product (the pages store weights in FP8, R2VA record
+first paragraph; this extension quantises the logits' operands too):
+
+  Q1  nearest OCP E4M3FN code of a value, ties to the even code, beyond 448 saturating
+  Q2  per-tensor power-of-two scale: 2^e with e the smallest integer such that
+      max|x| <= 448 * 2^e; Q and K are coded as Q1(x / 2^e) and O7 then runs on the
+      decoded values (code value times 2^e)
+
 and, as a fixed index producer beside the learned one:
 
   P1  the sliding frame-chunk window with boundary anchors   (VDN article, "The
@@ -269,8 +277,10 @@ def attend_rows(q_rows: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
 
 def attend_tile(q_bits, k_bits, v_bits, b: int, h: int, qtile: int, idx_row: np.ndarray,
                 tile: int, query: Tuple[int, int], segments, dense,
-                scale: Optional[float] = None):
-    """O7 for one (batch, head, query tile): returns (out [t, d], lse [t]) in float64."""
+                scale: Optional[float] = None, dq=bf16_bits_to_f64, dk=bf16_bits_to_f64):
+    """O7 for one (batch, head, query tile): returns (out [t, d], lse [t]) in float64.
+    dq / dk turn stored Q / K elements into values (bf16 bits by default; fp8_values for
+    E4M3FN codes)."""
     d = q_bits.shape[3]
     if scale is None or scale == 0.0:
         scale = 1.0 / math.sqrt(d)
@@ -279,8 +289,8 @@ def attend_tile(q_bits, k_bits, v_bits, b: int, h: int, qtile: int, idx_row: np.
     toks = attended_tokens(idx_row, tile, segments, dense)
     if toks.size == 0:
         raise ValueError("query tile attends to no keys")
-    qr = bf16_bits_to_f64(q_bits[b, q0:q1, h, :])
-    kr = bf16_bits_to_f64(k_bits[b, toks, h, :])
+    qr = dq(q_bits[b, q0:q1, h, :])
+    kr = dk(k_bits[b, toks, h, :])
     vr = bf16_bits_to_f64(v_bits[b, toks, h, :])
     return attend_rows(qr, kr, vr, scale)
 
@@ -303,8 +313,10 @@ def attend_all_keys(q_bits, k_bits, v_bits, b: int, h: int, rows: Tuple[int, int
 
 def attend(q_bits, k_bits, v_bits, idx: np.ndarray, tile: int, query: Tuple[int, int],
            segments, dense, scale: Optional[float] = None,
-           pairs: Optional[Iterable[Tuple[int, int, int]]] = None):
-    """O7 over a layer, or over the (b, h, query tile) triples in `pairs`.
+           pairs: Optional[Iterable[Tuple[int, int, int]]] = None,
+           dq=bf16_bits_to_f64, dk=bf16_bits_to_f64):
+    """O7 over a layer, or over the (b, h, query tile) triples in `pairs` (dq / dk as in
+    attend_tile).
 
     Returns dict {(b, h, qtile): (out [t, d], lse [t])}.
     """
@@ -315,8 +327,55 @@ def attend(q_bits, k_bits, v_bits, idx: np.ndarray, tile: int, query: Tuple[int,
     res = {}
     for (b, h, i) in pairs:
         res[(b, h, i)] = attend_tile(q_bits, k_bits, v_bits, b, h, i, idx[b, h, i], tile,
-                                     query, segments, dense, scale)
+                                     query, segments, dense, scale, dq, dk)
     return res
+
+
+# ----------------------------------------------------------------------------- Q1, Q2
+
+# codes 0x00 .. 0x7E: every non-negative finite E4M3FN value, in ascending order
+_E4M3_MAGS = _E4M3_TABLE[:127]
+
+
+def e4m3fn_round(x) -> np.ndarray:
+    """Q1: the E4M3FN code nearest to each float64 value (by definition: the closest of
+    the finite magnitudes; an exact tie goes to the even code, i.e. mantissa bit 0;
+    magnitudes at or beyond 448 give 448).  The sign bit is x's, so -0.0 and negative
+    values that round to zero give 0x80; NaN gives 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(_E4M3_MAGS, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = a - _E4M3_MAGS[lo]
+    d_hi = _E4M3_MAGS[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(a >= 448.0, 126, code)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def fp8_scale_exponent(amax: float) -> int:
+    """Q2: the smallest integer e with amax <= 448 * 2^e (0 for amax == 0)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = math.frexp(amax)[1] - 10
+    while 448.0 * 2.0 ** e < amax:
+        e += 1
+    return e
+
+
+def quantize_fp8(x_bits: np.ndarray) -> Tuple[np.ndarray, int]:
+    """Q2 on a bf16 tensor (all of it): (E4M3FN codes of x / 2^e, e)."""
+    x = bf16_bits_to_f64(x_bits)
+    e = fp8_scale_exponent(np.abs(x).max() if x.size else 0.0)
+    return e4m3fn_round(x * 2.0 ** -e), e
+
+
+def fp8_values(e: int):
+    """Decoder for attend / attend_tile: E4M3FN codes times 2^e, as float64."""
+    return lambda codes: dequant_e4m3fn(codes, e)
 
 
 # ----------------------------------------------------------------------------- T1, T2
