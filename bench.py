@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dense-equiv attention TFLOP/s + selector+attn ms/layer at 90/95% sparsity"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 
@@ -45,6 +46,8 @@ def parse():
                     help="skip timing selection + attention on every workload (field 'sweep')")
     ap.add_argument("--no-patterns", action="store_true",
                     help="skip the budget 16/32/64 and VDN window timings (field 'patterns')")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 Q.K^T path timing (field 'fp8qk')")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (byte-counter calibration)")
     return ap.parse_args()
@@ -404,6 +407,48 @@ def random_pattern(lay, kernel_reps, log):
             "actual_tflops_attn": round(fl / (med * 1e-3) / 1e12, 1)}
 
 
+def measure_fp8qk(lay, kernel_reps, log):
+    """The FP8 Q.K^T path on the same layer and index sets: Q and K quantised on the GPU
+    (E4M3FN, per-tensor power-of-two scale), then veda_sparse_attn_fp8qk.  Its first
+    product runs at the FP8 matrix rate and its second at the bf16 rate, so the peak it is
+    compared with is the harmonic mean of the two (equal flops in each product)."""
+    import torch
+    B, wl = lay.B, lay.wl
+    q8, qs = B.quantize_fp8(lay.L, lay.qd)
+    k8, ks = B.quantize_fp8(lay.L, lay.kd)
+    out8 = torch.zeros_like(lay.qd)
+
+    def quant():
+        B.quantize_fp8(lay.L, lay.qd, out=q8, scale=qs)
+        B.quantize_fp8(lay.L, lay.kd, out=k8, scale=ks)
+
+    def attn8():
+        B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, lay.idx, lay.dense, out=out8)
+
+    lay.select()
+    lay.attn()
+    quant()
+    attn8()
+    torch.cuda.synchronize()
+    q_ms, _, q_med = time_events(quant, kernel_reps)
+    a_ms, a_min, a_med = time_events(attn8, kernel_reps)
+    fl = lay.actual_flops(lay.idx.cpu().numpy())
+    q0, q1 = wl.query.start, wl.query.start + wl.query.length
+    diff = (out8[:, q0:q1].float() - lay.out[:, q0:q1].float()).abs()
+    mixed_peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+    tf = fl / (a_med * 1e-3) / 1e12
+    log(f"[{wl.name}] fp8 Q.K^T attention: {a_med:.3f} ms ({tf:.0f} TFLOP/s), quantising Q and K {q_med:.3f} ms")
+    res = {"attn_ms": round(a_ms, 4), "attn_ms_median": round(a_med, 4), "attn_ms_min": round(a_min, 4),
+           "quantize_qk_ms": round(q_med, 4), "actual_tflops_attn": round(tf, 1),
+           "mixed_peak_tflops": round(mixed_peak, 1), "frac_mixed_peak": round(tf / mixed_peak, 4),
+           "speedup_vs_bf16_attn": None,
+           "max_abs_vs_bf16_out": round(float(diff.max()), 5), "mean_abs_vs_bf16_out": round(float(diff.mean()), 6),
+           "kernel": f"sparse_attn_fp8qk_pingpong_kernel<{wl.d}>"}
+    del q8, k8, out8
+    torch.cuda.empty_cache()
+    return res
+
+
 def sdpa_dense(lay, reps, log):
     """torch's scaled_dot_product_attention (flash / memory-efficient backends only) at the
     dense shape of the layer, every token a key: context for the dense baseline."""
@@ -542,6 +587,10 @@ def main():
     patterns = None if args.no_patterns else measure_patterns(lay, args.kernel_reps, log)
     if patterns is not None:
         patterns["random_indices"] = random_pattern(lay, args.kernel_reps, log)
+    fp8qk = None
+    if not args.no_fp8 and lay.wl.tile == 128:
+        fp8qk = measure_fp8qk(lay, args.kernel_reps, log)
+        fp8qk["speedup_vs_bf16_attn"] = round(res["attn_ms_median"] / fp8qk["attn_ms_median"], 3)
     peaks = device_peaks(log)
     also = None
     if args.also and args.also != "none" and args.also != args.workload:
@@ -616,6 +665,7 @@ def main():
                      "kernel": attn_kernel, "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
         "cpu_baseline": cpu,
         "patterns": patterns,
+        "fp8qk": fp8qk,
         "also": also,
         "sweep": sweep,
         "detail": res,

@@ -89,6 +89,9 @@ def _load():
         "veda_sparse_attn": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                             ctypes.c_float, P, P, P]),
         "veda_dequant_fp8_e4m3": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
+        "veda_sparse_attn_fp8qk": (ctypes.c_int, [L, P, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+                                                  ctypes.c_float, P, P, P]),
+        "veda_quantize_fp8_e4m3": (ctypes.c_int, [L, P, P, P, P]),
         "veda_sparse_attn_check": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                                   ctypes.c_float, P]),
         "veda_layer_attn": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
@@ -130,11 +133,12 @@ def exported_symbols():
                         "veda_window_indices", "veda_block_mass", "veda_block_recall",
                         "veda_st_open", "veda_st_close", "veda_st_count", "veda_st_info",
                         "veda_st_find", "veda_st_read", "veda_st_metadata_count",
-                        "veda_st_metadata_at", "veda_mfma_peak")]
+                        "veda_st_metadata_at", "veda_mfma_peak", "veda_sparse_attn_fp8qk",
+                        "veda_quantize_fp8_e4m3")]
 
 
 # VEDA_ABI_VERSION of include/veda.h that this binding marshals for
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def abi_version() -> int:
@@ -291,6 +295,61 @@ def sparse_attn(layer: Layer, q, k, v, idx, dense: Sequence[Tuple[int, int]] = (
     st = _load().veda_sparse_attn(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), arr, n,
                                   float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "veda_sparse_attn")
+    return (out, lse) if want_lse else out
+
+
+def _check_fp8(layer: Layer, *xs):
+    for x in xs:
+        if x.dtype != torch.uint8 or not x.is_cuda:
+            raise ValueError("FP8 Q/K must be uint8 device tensors of E4M3FN codes")
+        if strides_of(x) != (layer.stride_b, layer.stride_n, layer.stride_h):
+            raise ValueError("tensor strides differ from the layer's strides")
+        if tuple(x.shape) != (layer.B, layer.n_tokens, layer.H, layer.d):
+            raise ValueError("tensor shape differs from the layer")
+
+
+def _check_scale(*xs):
+    for x in xs:
+        if x.dtype != torch.float32 or not x.is_cuda or x.numel() < 1:
+            raise ValueError("FP8 scales must be float32 device tensors (first element used)")
+
+
+def quantize_fp8(layer: Layer, x, out=None, scale=None, stream=None):
+    """bf16 Q or K -> (E4M3FN codes uint8 with x's shape and strides, float32 [1] scale 2^e)."""
+    _check_qkv(layer, x)
+    if out is None:
+        out = torch.empty_strided(tuple(x.shape), tuple(x.stride()), dtype=torch.uint8, device=x.device)
+    _check_fp8(layer, out)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check_scale(scale)
+    st = _load().veda_quantize_fp8_e4m3(ctypes.byref(layer), _ptr(x), _ptr(out), _ptr(scale), _stream(stream))
+    _check(st, "veda_quantize_fp8_e4m3")
+    return out, scale
+
+
+def sparse_attn_fp8qk(layer: Layer, q8, k8, v, q_scale, k_scale, idx, dense: Sequence[Tuple[int, int]] = (),
+                      scale: float = 0.0, out=None, want_lse: bool = False, stream=None):
+    """veda_sparse_attn with E4M3FN Q and K (codes and per-tensor scales as quantize_fp8 returns
+    them); v bf16.  Returns out (bf16, v's shape) [and lse fp32 [B, H, query.len]]."""
+    _check_fp8(layer, q8, k8)
+    _check_qkv(layer, v)
+    _check_scale(q_scale, k_scale)
+    if out is None:
+        out = torch.zeros_like(v)
+    else:
+        _check_qkv(layer, out)
+    lse = torch.empty((layer.B, layer.H, layer.query.len), dtype=torch.float32, device=v.device) \
+        if want_lse else None
+    if idx is not None:
+        if idx.dtype != torch.int32 or not idx.is_contiguous() or \
+                tuple(idx.shape) != (layer.B, layer.H, layer.Tq, layer.Ktot):
+            raise ValueError("idx must be contiguous int32 [B, H, Tq, Ktot]")
+    arr, n = dense_ranges(list(dense))
+    st = _load().veda_sparse_attn_fp8qk(ctypes.byref(layer), _ptr(q8), _ptr(k8), _ptr(v), _ptr(q_scale),
+                                        _ptr(k_scale), _ptr(idx), arr, n, float(scale), _ptr(out), _ptr(lse),
+                                        _stream(stream))
+    _check(st, "veda_sparse_attn_fp8qk")
     return (out, lse) if want_lse else out
 
 

@@ -255,6 +255,38 @@ int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, cons
                                              (hipStream_t)stream));
 }
 
+int veda_sparse_attn_fp8qk(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const void* v,
+                           const float* q_scale, const float* k_scale, const int32_t* idx,
+                           const veda_range* dense, int32_t n_dense, float scale, void* out,
+                           float* lse_opt, void* stream) {
+  veda::DenseDev DD{};
+  int st = sparse_attn_check(layer, q8, k8, v, idx, dense, n_dense, scale, out, &DD);
+  if (st != VEDA_OK) return st;
+  if (!q_scale || !k_scale) return VEDA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+    return VEDA_EINVAL;
+  // one-byte rows: 16-byte loads need 16-element strides
+  if ((layer->stride_b % 16) || (layer->stride_n % 16) || (layer->stride_h % 16)) return VEDA_EINVAL;
+  if (lse_opt && !aligned16(lse_opt)) return VEDA_EINVAL;
+  if (layer->tile != 128) return VEDA_EUNSUPPORTED;
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) return VEDA_OK;
+  if (!veda::two_group_fits(D, DD)) return VEDA_EUNSUPPORTED;
+  if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
+  return hip_status(veda::launch_sparse_attn_fp8qk(D, DD, q8, k8, v, idx, scale, q_scale, k_scale, out,
+                                                   lse_opt, (hipStream_t)stream));
+}
+
+int veda_quantize_fp8_e4m3(const veda_layer* layer, const void* x, uint8_t* x8, float* scale,
+                           void* stream) {
+  int st = check_layer(layer, false);
+  if (st != VEDA_OK) return st;
+  if (!x || !x8 || !scale) return VEDA_EINVAL;
+  if (!aligned16(x) || !aligned16(x8) || (reinterpret_cast<uintptr_t>(scale) & 3u)) return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  return hip_status(veda::launch_quantize_fp8(D, layer->n_tokens, x, x8, scale, (hipStream_t)stream));
+}
+
 int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
                     const void* wq, const void* wk, const veda_range* dense, int32_t n_dense,
                     const veda_range* dense_queries, int32_t n_dense_queries, float scale,

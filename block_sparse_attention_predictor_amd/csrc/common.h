@@ -49,6 +49,17 @@ hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float*
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& D, const void* q, const void* k,
                               const void* v, const int32_t* idx, float scale, void* out,
                               float* lse, hipStream_t s);
+// Q and K as E4M3FN codes (same element strides as the bf16 tensors, one byte each) with
+// per-tensor scales in device memory; V, O as in launch_sparse_attn.  Needs 128-row tiles
+// and a block list within the two-group kernel's table (two_group_fits).
+hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& D, const void* q8, const void* k8,
+                                    const void* v, const int32_t* idx, float scale, const float* q_scale,
+                                    const float* k_scale, void* out, float* lse, hipStream_t s);
+bool two_group_fits(const LayerDev& L, const DenseDev& D);
+// bf16 tensor [B, n_tokens, H, d] (layer strides) -> E4M3FN codes at the same element
+// offsets, with the per-tensor power-of-two scale written to *scale (device float).
+hipError_t launch_quantize_fp8(const LayerDev& L, int64_t n_tokens, const void* x, uint8_t* x8,
+                                float* scale, hipStream_t s);
 hipError_t launch_dequant_e4m3(const uint8_t* src, void* dst, int64_t n, int32_t pow2_exp,
                                hipStream_t s);
 

@@ -54,6 +54,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 typedef const __attribute__((address_space(4))) int32_t* const_i32_t;
@@ -500,19 +502,28 @@ __device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseD
 // the barrier); every wave ends each slot by waiting for the loads it issued two slots
 // earlier.  The two partial results (each with its own running maximum) are merged
 // through LDS at the end.
-template <int D>
-__global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
-    LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+//
+// K8: Q and K are FP8 (E4M3FN) codes and the first product runs on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales); V, P and the second product stay
+// bf16.  A K row is then d bytes: the K stages use the first half of their space, a
+// block's K DMA is half as many loads, and S^T takes 2 * d / 64 products instead of d / 8.
+template <int D, bool K8>
+__device__ __forceinline__ void pingpong_attn(
+    const LayerDev& L, const DenseDev& DN, const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ q,
+    const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int by_heads) {
+  using KT = std::conditional_t<K8, uint8_t, uint16_t>;
   constexpr int NW = 4;                       // waves per group
   constexpr int NT = 64 * NW;                 // threads per group
-  constexpr int CPR = D / 8;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per bf16 row
   constexpr int SLOTS = KB * CPR;
-  constexpr int LPT = SLOTS / NT;             // DMA loads per thread per tensor and block
+  constexpr int LPT = SLOTS / NT;             // V DMA loads per thread per block
+  constexpr int KCPR = K8 ? D / 16 : CPR;     // 16-byte chunks per K row
+  constexpr int LPK = KB * KCPR / NT;         // K DMA loads per thread per block
   constexpr int NPV = (D / 32) * 4;           // PV products per block
-  constexpr int NS = D / 8;                   // S^T products per block
-  static_assert(SLOTS % NT == 0 && 2 * LPT < 16, "block split");
+  constexpr int NS = K8 ? 2 * (D / 64) : D / 8;   // S^T products per block
+  static_assert(SLOTS % NT == 0 && (KB * KCPR) % NT == 0 && LPK + LPT < 16, "block split");
 
   // one array per group: K stage 0, K stage 1, V stage 0, V stage 1 (the DMA is issued
   // from inline assembly, so no compiler-inserted wait depends on their aliasing)
@@ -540,16 +551,27 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
 
   const int64_t my_q = q_first + wave * 32 + l32;
   const bool q_ok = my_q < q_end;
-  bf16x8 qv[D / 16];
-  {
+  // Q^T operand: bf16, 8 head-dim values per product; FP8, 32 bytes per product
+  // (bytes 64 ks + 32 hi .. +31 of the row, the same bytes the K operand reads)
+  bf16x8 qv[K8 ? 1 : D / 16];
+  i32x8 qv8[K8 ? D / 64 : 1];
+  if constexpr (K8) {
+    const uint8_t* qp = q + head_off + (q_ok ? my_q : q_first) * L.sn + 32 * hi;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      const uint4 w0 = q_ok ? *reinterpret_cast<const uint4*>(qp + 64 * ks) : make_uint4(0, 0, 0, 0);
+      const uint4 w1 = q_ok ? *reinterpret_cast<const uint4*>(qp + 64 * ks + 16) : make_uint4(0, 0, 0, 0);
+      qv8[ks] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+    }
+  } else {
     const uint16_t* qp = q + head_off + (q_ok ? my_q : q_first) * L.sn + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       uint4 w = q_ok ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
       qv[kk] = __builtin_bit_cast(bf16x8, w);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q is in registers before any DMA is issued
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): Q is in registers before any DMA is issued
 
   if (tid < 64) {
     const int n = build_block_table(L, DN, idx_row, lane, stab);
@@ -558,17 +580,26 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
   __syncthreads();
   const int nblk = __builtin_amdgcn_readfirstlane(snblk);
 
-  auto dma_row = [&](int i) { return ((wave * LPT + i) * 64 + lane) / CPR; };
-  auto dma_col = [&](int i, bool is_v) {
-    const int r = dma_row(i);
-    const int pc = ((wave * LPT + i) * 64 + lane) % CPR;
-    return (pc ^ (is_v ? swz_v<CPR>(r) : swz_k<CPR>(r))) * 8;
+  // K row swizzle: bf16 rows (256 or 128 bytes) as in the single-pipeline kernel; FP8
+  // rows (128 or 64 bytes) by row pair (quad for 64 bytes), so that the 16 rows one
+  // 16-lane operand read touches cover every 16-byte bank group once
+  auto kswz = [](int r) {
+    if constexpr (K8) return (r >> (KCPR == 8 ? 1 : 2)) & (KCPR - 1);
+    else return swz_k<CPR>(r);
   };
-  uint32_t koff[LPT], voff[LPT];
+  // load i of this thread fills 16-byte LDS slot (wave * loads + i) * 64 + lane
+  uint32_t koff[LPK], voff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPK; ++i) {
+    const int slot = (wave * LPK + i) * 64 + lane;
+    const int r = slot / KCPR;
+    koff[i] = (uint32_t)((int64_t)r * L.sn * (int64_t)sizeof(KT) + (((slot % KCPR) ^ kswz(r)) << 4));
+  }
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    koff[i] = (uint32_t)(((int64_t)dma_row(i) * L.sn + dma_col(i, false)) * 2);
-    voff[i] = (uint32_t)(((int64_t)dma_row(i) * L.sn + dma_col(i, true)) * 2);
+    const int slot = (wave * LPT + i) * 64 + lane;
+    const int r = slot / CPR;
+    voff[i] = (uint32_t)((int64_t)r * L.sn * 2 + (((slot % CPR) ^ swz_v<CPR>(r)) << 4));
   }
   const char* kbase = reinterpret_cast<const char*>(k + head_off);
   const char* vbase = reinterpret_cast<const char*>(v + head_off);
@@ -582,12 +613,18 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
                  : "s"(lds_addr), "v"(off), "s"(g)
                  : "memory", "m0");
   };
-  auto dma = [&](const char* base, const uint32_t* off, const Block& blk, uint16_t* dst) {
-    const char* g = base + blk.start * L.sn * 2;
-    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t)(reinterpret_cast<char*>(dst) + wave * LPT * 1024);
+  // a block's K (IS_V = 0) or V (IS_V = 1) rows; rows past a partial block's end load
+  // its last row again
+  auto dma = [&](auto is_v, const char* base, const uint32_t* off, const Block& blk, uint16_t* dst) {
+    constexpr bool IS_V = decltype(is_v)::value;
+    constexpr int NL = IS_V ? LPT : LPK;
+    constexpr int CP = IS_V ? CPR : KCPR;
+    constexpr int EB = IS_V ? 2 : (int)sizeof(KT);
+    const char* g = base + blk.start * L.sn * EB;
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t)(reinterpret_cast<char*>(dst) + wave * NL * 1024);
     if (blk.n == KB) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) {
+      for (int i = 0; i < NL; ++i) {
         uint32_t o = off[i];
         asm volatile("" : "+v"(o));
         dma1(g, o, l0 + i * 1024);
@@ -596,23 +633,26 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
       int ln = lane;
       asm volatile("" : "+v"(ln) : : "memory");
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int r = ((wave * LPT + i) * 64 + ln) / CPR;
+      for (int i = 0; i < NL; ++i) {
+        const int r = ((wave * NL + i) * 64 + ln) / CP;
         const int rc = r < blk.n ? r : blk.n - 1;
-        dma1(g, off[i] - (uint32_t)((r - rc) * (int)L.sn * 2), l0 + i * 1024);
+        dma1(g, off[i] - (uint32_t)((r - rc) * (int)L.sn * EB), l0 + i * 1024);
       }
     }
   };
+  const std::integral_constant<bool, false> kK{};
+  const std::integral_constant<bool, true> kV{};
   // workgroup barrier without a memory fence (outstanding DMA is waited for explicitly)
   auto barrier = []() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_barrier" : : : "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // wait until at most n of this wave's DMA loads are outstanding (n in {0, LPT, 2 LPT})
+  // wait until at most n of this wave's DMA loads are outstanding (n in {0, LPK, LPT, LPK + LPT})
   auto wait_vm = [](int n) {
-    if (n == 2 * LPT) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPT));
+    if (n == LPK + LPT) __builtin_amdgcn_s_waitcnt(0x0F70 | (LPK + LPT));
     else if (n == LPT) __builtin_amdgcn_s_waitcnt(0x0F70 | LPT);
+    else if (n == LPK) __builtin_amdgcn_s_waitcnt(0x0F70 | LPK);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
   };
 
@@ -643,11 +683,20 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
     // operand addresses: group base plus the lane's swizzled offset for every K column
     // step and every V column block; stage and row offsets are instruction immediates
     const uint32_t gbase = (uint32_t)(uintptr_t)(lds_void_t)Gb;
-    uint32_t kA[D / 16], vA[D / 32];
+    uint32_t kA[K8 ? 2 * (D / 64) : D / 16], vA[D / 32];
+    if constexpr (K8) {
+      // FP8: product ks reads the 16-byte chunks 4 ks + 2 hi and 4 ks + 2 hi + 1 of row l32
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kA[kk] = gbase + (kR ^ (kk << 5));
-      asm volatile("" : "+v"(kA[kk]));
+      for (int c = 0; c < 2 * (D / 64); ++c) {
+        kA[c] = gbase + (uint32_t)l32 * D + ((uint32_t)((4 * (c >> 1) + 2 * hi + (c & 1)) ^ kswz(l32)) << 4);
+        asm volatile("" : "+v"(kA[c]));
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        kA[kk] = gbase + (kR ^ (kk << 5));
+        asm volatile("" : "+v"(kA[kk]));
+      }
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -673,11 +722,11 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
     Block nx1 = entry(2 + GRP);               // c_{j+1}
     Block nx2 = entry(4 + GRP);               // c_{j+2}
     Block prev{0, 0};                         // c_{j-1}
-    if (cur.n > 0) dma(kbase, koff, cur, Ks0);
-    if (nx1.n > 0) dma(kbase, koff, nx1, Ks1);
+    if (cur.n > 0) dma(kK, kbase, koff, cur, Ks0);
+    if (nx1.n > 0) dma(kK, kbase, koff, nx1, Ks1);
     int np = 0;                               // this wave's loads issued in the previous phase
     if (cur.n > 0) {
-      dma(vbase, voff, cur, Vs0);
+      dma(kV, vbase, voff, cur, Vs0);
       np = LPT;
     }
     wait_vm(np);                              // K(c_0) and K(c_1) landed
@@ -718,12 +767,23 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
           va[db][c] = __builtin_bit_cast(bf16x8, both);
         }
     };
-    auto read_k = [&](int ST, bf16x8 (&ka)[2][D / 16]) {   // K stage ST
+    auto read_k = [&](int ST, auto& ka) {   // K stage ST, bf16: ka[2][D / 16]
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
           ka[mb][kk] = *(lds_bf16x8_t)(uintptr_t)(kA[kk] + ST * KB * D * 2 + mb * 32 * D * 2);
+    };
+    typedef __attribute__((address_space(3))) const i32x4* lds_i32x4_t;
+    auto read_k8 = [&](int ST, auto& ka) {  // K stage ST, FP8: ka[2][D / 64], two chunks each
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const i32x4 a = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks] + ST * KB * D * 2 + mb * 32 * D);
+          const i32x4 b = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks + 1] + ST * KB * D * 2 + mb * 32 * D);
+          ka[mb][ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
     };
     auto mul_pv = [&](const bf16x8 (&va)[D / 32][4]) {
 #pragma unroll
@@ -732,7 +792,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
         for (int c = 0; c < 4; ++c)
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[c], o[db], 0, 0, 0);
     };
-    auto mul_s = [&](const bf16x8 (&ka)[2][D / 16]) {
+    auto mul_s = [&](const auto& ka) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -743,6 +803,18 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
         for (int mb = 0; mb < 2; ++mb)
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mb][kk], qv[kk], s[mb], 0, 0, 0);
     };
+    // FP8 E4M3 operands (format code 0 for A and B), unit block scales (E8M0 code 127)
+    auto mul_s8 = [&](const auto& ka) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[mb][ks], qv8[ks], s[mb], 0, 0, 0, 127, 0, 127);
+    };
 
     // products slot of c_j: PV of c_{j-1} (V stage (j-1)%2), S^T of c_j (K stage j%2).
     // Always both, with no branch: a missing c_{j-1} has P = 0 against finite V stage
@@ -751,33 +823,56 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
     auto mphase = [&](auto stage) {
       constexpr int ST = decltype(stage)::value;
       bf16x8 va[D / 32][4];
-      bf16x8 ka[2][D / 16];
       read_v(1 - ST, va);
-      read_k(ST, ka);
-      mul_pv(va);
-      mul_s(ka);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      // V reads (2 per PV product), then K reads; 8 reads go first, then each PV
+      // product is followed by two reads, the last four by one
+      if constexpr (K8) {
+        i32x8 ka[2][D / 64];
+        read_k8(ST, ka);
+        mul_pv(va);
+        mul_s8(ka);
+        constexpr int NKR = 2 * NS;             // two 16-byte reads per S^T product
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int i = 0; i < NPV - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
+        for (int i = 0; i < NPV - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (NKR > 4) __builtin_amdgcn_sched_group_barrier(0x100, NKR - 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+      } else {
+        bf16x8 ka[2][D / 16];
+        read_k(ST, ka);
+        mul_pv(va);
+        mul_s(ka);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int i = 0; i < NS - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < NPV - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NS - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       __builtin_amdgcn_sched_barrier(0);
       int nc = 0;
       if (xo.n > 0) {
         // group 1 fills group 0's V stage (j+1)%2, group 0 fills group 1's V stage j%2
-        dma(vbase, voff, xo, Go + (2 + (GRP ? 1 - ST : ST)) * KB * D);
+        dma(kV, vbase, voff, xo, Go + (2 + (GRP ? 1 - ST : ST)) * KB * D);
         nc = LPT;
       }
       wait_vm(nc + np);                       // loads of two phases ago have landed
@@ -796,8 +891,8 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
       const int2 eo = io < nblk ? stab[io] : make_int2(0, 0);
       int nc = 0;
       if (nx2.n > 0) {
-        dma(kbase, koff, nx2, Kf);
-        nc = LPT;
+        dma(kK, kbase, koff, nx2, Kf);
+        nc = LPK;
       }
       if (cur.n > 0) {
         const int n = cur.n;
@@ -949,23 +1044,30 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
+    LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, false>(L, DN, q, k, v, idx, scale_log2, out, lse, by_heads);
+}
+
+// Q and K as FP8 codes with per-tensor scales (device floats): logits are
+// scale * q_scale * k_scale * <q8, k8>.
+template <int D>
+__global__ __launch_bounds__(512, 1) void sparse_attn_fp8qk_pingpong_kernel(
+    LayerDev L, DenseDev DN, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, true>(L, DN, q, k, v, idx, scale_log2 * q_scale[0] * k_scale[0], out, lse, by_heads);
+}
+
 }  // namespace
 
-hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void* q, const void* k,
-                              const void* v, const int32_t* idx, float scale, void* out, float* lse,
-                              hipStream_t s) {
-  const int by_heads = idx == nullptr && L.B * L.H >= 8;
-  const int64_t per_xcd = (L.Tq + 7) / 8;
-  const int64_t nwork = by_heads ? ((int64_t)L.B * L.H + 7) / 8 * 8 * L.Tq : (int64_t)L.B * L.H * per_xcd * 8;
-  if (nwork > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const float scale_log2 = scale * 1.44269504088896340736f;
-  dim3 grid((unsigned)nwork);
-  auto qq = static_cast<const uint16_t*>(q);
-  auto kk = static_cast<const uint16_t*>(k);
-  auto vv = static_cast<const uint16_t*>(v);
-  auto oo = static_cast<uint16_t*>(out);
-  // 128-row tiles take the two-group kernel when the row's block list fits its LDS table
-  // and every token index fits the table's 32-bit entries
+// 128-row tiles take the two-group kernel when the row's block list fits its LDS table
+// and every token index fits the table's 32-bit entries
+bool two_group_fits(const LayerDev& L, const DenseDev& DN) {
   int64_t bound = (int64_t)L.Ktot * (L.tile / KB);
   int64_t last = 0;
   for (int i = 0; i < DN.n; ++i) {
@@ -974,7 +1076,32 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void*
   }
   for (int i = 0; i < L.n_seg; ++i)
     last = L.seg[i].start + L.seg[i].len > last ? L.seg[i].start + L.seg[i].len : last;
-  const bool two_group = L.tile == 128 && bound <= kTabCap && last < ((int64_t)1 << 31);
+  return L.tile == 128 && bound <= kTabCap && last < ((int64_t)1 << 31);
+}
+
+namespace {
+bool grid_of(const LayerDev& L, const int32_t* idx, dim3& grid, int& by_heads) {
+  by_heads = idx == nullptr && L.B * L.H >= 8;
+  const int64_t per_xcd = (L.Tq + 7) / 8;
+  const int64_t nwork = by_heads ? ((int64_t)L.B * L.H + 7) / 8 * 8 * L.Tq : (int64_t)L.B * L.H * per_xcd * 8;
+  if (nwork > 0x7FFFFFFF) return false;
+  grid = dim3((unsigned)nwork);
+  return true;
+}
+}  // namespace
+
+hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void* q, const void* k,
+                              const void* v, const int32_t* idx, float scale, void* out, float* lse,
+                              hipStream_t s) {
+  dim3 grid;
+  int by_heads;
+  if (!grid_of(L, idx, grid, by_heads)) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  auto qq = static_cast<const uint16_t*>(q);
+  auto kk = static_cast<const uint16_t*>(k);
+  auto vv = static_cast<const uint16_t*>(v);
+  auto oo = static_cast<uint16_t*>(out);
+  const bool two_group = two_group_fits(L, DN);
   if (two_group && L.d == 128)
     hipLaunchKernelGGL((sparse_attn_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
@@ -993,6 +1120,26 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void*
   else
     hipLaunchKernelGGL((sparse_attn_kernel<64, 2, 32>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& DN, const void* q8, const void* k8,
+                                    const void* v, const int32_t* idx, float scale, const float* q_scale,
+                                    const float* k_scale, void* out, float* lse, hipStream_t s) {
+  dim3 grid;
+  int by_heads;
+  if (!grid_of(L, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  auto qq = static_cast<const uint8_t*>(q8);
+  auto kk = static_cast<const uint8_t*>(k8);
+  auto vv = static_cast<const uint16_t*>(v);
+  auto oo = static_cast<uint16_t*>(out);
+  if (L.d == 128)
+    hipLaunchKernelGGL((sparse_attn_fp8qk_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
+                       scale_log2, q_scale, k_scale, oo, lse, by_heads);
+  else
+    hipLaunchKernelGGL((sparse_attn_fp8qk_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
+                       scale_log2, q_scale, k_scale, oo, lse, by_heads);
   return hipGetLastError();
 }
 

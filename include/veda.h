@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 2
+#define VEDA_ABI_VERSION 3
 #define VEDA_MAX_SEGMENTS 4
 #define VEDA_MAX_DENSE 8
 #define VEDA_MAX_KEY_TILES 8192   /* sum over segments of T_s accepted by selection */
@@ -181,6 +181,38 @@ int veda_select(const veda_layer* layer, const void* q, const void* k,
 int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
                      const int32_t* idx, const veda_range* dense, int32_t n_dense,
                      float scale, void* out, float* lse_opt, void* stream);
+
+/*
+ * FP8 variant of veda_sparse_attn's first product (row f4 of the scope: the pages'
+ * FP8 paths, R2VA record first paragraph and the VDN article's fp8 transformer, store
+ * weights in FP8; this extends it to the logits, which the pages do not describe).
+ * q8 and k8 hold OCP E4M3FN codes of Q and K at the same element offsets as the bf16
+ * tensors (layer strides, one byte per element; strides must be multiples of 16),
+ * each with a per-tensor scale in device memory (one float, as veda_quantize_fp8_e4m3
+ * writes it).  Logits are
+ *     scale * q_scale * k_scale * sum_c e4m3(q8[b,n,h,c]) * e4m3(k8[b,m,h,c])
+ * on the FP8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation; its
+ * sum of 64 products is not exact: measured within 2^-12 of the largest product).
+ * Softmax, P (bf16) . V (bf16) and every other argument are as in veda_sparse_attn.
+ * Needs 128-row tiles and at most 3072 64-key blocks per query tile (selected tiles
+ * plus dense ranges); else VEDA_EUNSUPPORTED.
+ */
+int veda_sparse_attn_fp8qk(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const void* v,
+                           const float* q_scale, const float* k_scale, const int32_t* idx,
+                           const veda_range* dense, int32_t n_dense, float scale, void* out,
+                           float* lse_opt, void* stream);
+
+/*
+ * Per-tensor FP8 quantisation for veda_sparse_attn_fp8qk: x is a bf16 tensor
+ * [B, n_tokens, H, d] with the layer's strides (every token, not only the query rows),
+ * x8 receives E4M3FN codes at the same element offsets (one byte each, 16-byte
+ * aligned), and *scale (device float) the power of two 2^e with e the smallest integer
+ * such that max|x| <= 448 * 2^e (2^0 for an all-zero x).  x8 = nearest E4M3FN value of
+ * x / 2^e, ties to the even code, sign kept (-0 -> 0x80); the division is exact and no
+ * code saturates.  Four launches on `stream`; x must be finite.
+ */
+int veda_quantize_fp8_e4m3(const veda_layer* layer, const void* x, uint8_t* x8, float* scale,
+                           void* stream);
 
 /*
  * Host-only check of a veda_sparse_attn call: returns the status veda_sparse_attn

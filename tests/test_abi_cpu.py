@@ -37,7 +37,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert Bnd.abi_version() == 2 == Bnd.ABI_VERSION
+    assert Bnd.abi_version() == 3 == Bnd.ABI_VERSION
     for code in range(-8, 1):
         assert Bnd.status_string(code) and "unknown" not in Bnd.status_string(code)
     assert "unknown" in Bnd.status_string(-99)
