@@ -253,3 +253,34 @@ def test_package_entry_points_resolve():
     import __graft_entry__ as entry
     assert callable(pkg.build) and callable(entry.build) and callable(entry.smoke)
     assert pkg.VedaError is Bnd.VedaError
+
+
+def test_fp8_entry_points_reject_before_device_calls():
+    lib = Bnd._load()
+    L = _layer()
+    fake = ctypes.c_void_p(0x10000)
+    dense, nd = Bnd.dense_ranges([(133056, 512), (133568, 256), (133824, 1024)])
+    args = lambda qs, ks: (ctypes.byref(L), fake, fake, fake, qs, ks, fake, dense, nd, 0.0, fake, None, None)
+    # missing or misaligned scales
+    assert lib.veda_sparse_attn_fp8qk(*args(None, fake)) == -1
+    assert lib.veda_sparse_attn_fp8qk(*args(fake, ctypes.c_void_p(0x10002))) == -1
+    # one-byte rows need strides that are multiples of 16 elements
+    L.stride_h = 136
+    L.stride_n = 136 * 40
+    L.stride_b = L.stride_n * L.n_tokens
+    assert lib.veda_sparse_attn_fp8qk(*args(fake, fake)) == -1
+    # 64-row tiles and block lists beyond the two-group kernel's table are not supported
+    L = _layer(tile=64)
+    assert lib.veda_sparse_attn_fp8qk(*args(fake, fake)) == -2
+    wl = I.WORKLOADS["t2v14s"]
+    Lb = Bnd.layer_from_workload(wl)
+    Lb.budget[0] = 4096                          # every tile: 5482 + 40 blocks per query tile
+    big, nb = Bnd.dense_ranges([(r.start, r.length) for r in wl.dense])
+    assert lib.veda_sparse_attn_fp8qk(ctypes.byref(Lb), fake, fake, fake, fake, fake, fake, big, nb, 0.0, fake,
+                                      None, None) == -2
+    # quantiser: null pointers, misaligned codes or scale
+    L = _layer()
+    assert lib.veda_quantize_fp8_e4m3(ctypes.byref(L), None, fake, fake, None) == -1
+    assert lib.veda_quantize_fp8_e4m3(ctypes.byref(L), fake, ctypes.c_void_p(0x10008), fake, None) == -1
+    assert lib.veda_quantize_fp8_e4m3(ctypes.byref(L), fake, fake, ctypes.c_void_p(0x10001), None) == -1
+    assert lib.veda_quantize_fp8_e4m3(ctypes.byref(_layer(d=96)), fake, fake, fake, None) == -2
