@@ -12,7 +12,9 @@
 //    key blocks and alternate products and softmax slot by slot (see its comment);
 //  * sparse_attn_kernel (64-row tiles with 32-key blocks, which lets two workgroups'
 //    waves share each SIMD; and 128-row rows whose block list exceeds the two-group
-//    kernel's LDS table): tile/32 waves, one pipeline.
+//    kernel's LDS table): tile/32 waves, one pipeline;
+//  * sparse_attn_fp8qk_pingpong_kernel: the two-group kernel with Q and K as FP8
+//    (E4M3FN) codes and the first product on the FP8 matrix cores.
 //
 // Memory path (gfx950):
 //  * K and V rows go HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per
