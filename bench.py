@@ -541,11 +541,15 @@ def cpu_baseline(lay, log, budget_s=20.0):
 
 def attention_kernel_name(wl):
     """The attention kernel the library launches for this layer: the two-group kernel for
-    128-row tiles whose key-block list fits its 3072-entry LDS table, else the single-pipeline one."""
-    blocks = sum(min(s.budget, -(-s.length // wl.tile)) for s in wl.segments) * (wl.tile // 64)
-    blocks += sum(-(-r.length // 64) for r in wl.dense)
+    128-row tiles whose 64-key block list fits its 3072-entry LDS table, its paired form
+    for 64-row tiles whose 32-key block list fits 1536 entries, else the single-pipeline one."""
+    kbk = 64 if wl.tile == 128 else 32
+    blocks = sum(min(s.budget, -(-s.length // wl.tile)) for s in wl.segments) * (wl.tile // kbk)
+    blocks += sum(-(-r.length // kbk) for r in wl.dense)
     if wl.tile == 128 and blocks <= 3072:
         return f"sparse_attn_pingpong_kernel<{wl.d}>"
+    if wl.tile == 64 and blocks <= 1536:
+        return f"sparse_attn_pingpong_pair_kernel<{wl.d}>"
     return f"sparse_attn_kernel<{wl.d}, {wl.tile // 32}, {32 if wl.tile == 64 else 64}>"
 
 

@@ -5,14 +5,17 @@
 // first paragraph: the selected reference and video tiles are attended per
 // query tile and head, while text, VLM conditioning and audio stay dense.
 //
-// One workgroup computes one (b, h, query tile).  Keys stream through LDS in blocks
-// of 64 tokens (32 for 64-row tiles): first the tiles named by the index row (gathered
-// by id), then every dense range, cut into blocks.  Two kernels share the math below:
+// One workgroup computes one (b, h, query tile), or two 64-row tiles.  Keys stream
+// through LDS in blocks of 64 tokens (32 for 64-row tiles): first the tiles named by the
+// index row (gathered by id), then every dense range, cut into blocks.  The kernels
+// share the math below:
 //  * sparse_attn_pingpong_kernel (128-row tiles): two groups of four waves split the
 //    key blocks and alternate products and softmax slot by slot (see its comment);
-//  * sparse_attn_kernel (64-row tiles with 32-key blocks, which lets two workgroups'
-//    waves share each SIMD; and 128-row rows whose block list exceeds the two-group
-//    kernel's LDS table): tile/32 waves, one pipeline;
+//  * sparse_attn_pingpong_pair_kernel (64-row tiles): the same, with two query tiles per
+//    workgroup, each half of a group streaming its own tile's 32-key blocks;
+//  * sparse_attn_kernel (rows whose block list exceeds the two-group tables):
+//    tile/32 waves, one pipeline (64-row tiles with 32-key blocks and four workgroups
+//    per CU);
 //  * sparse_attn_fp8qk_pingpong_kernel: the two-group kernel with Q and K as FP8
 //    (E4M3FN) codes and the first product on the FP8 matrix cores.
 //
@@ -132,19 +135,23 @@ __device__ __forceinline__ int swz_v(int row) { return (row & 3) * (CPR / 4); }
 //  * by heads (no index: every tile of every segment, e.g. the dense query rows of a
 //    layer): every XCD takes whole heads, so the query tiles of one head, which read the
 //    same keys in the same order, run side by side and share that XCD's L2.
+// n is the number of work items per (b, h): query tiles, or pairs of them.
 // Returns false for a padding workgroup (a uniform exit before any barrier).
-__device__ __forceinline__ bool work_item(const LayerDev& L, int by_heads, int& bh, int& qt) {
+__device__ __forceinline__ bool work_item(const LayerDev& L, int n, int by_heads, int& bh, int& it) {
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   if (by_heads) {
-    bh = (slot / L.Tq) * 8 + xcd;
-    qt = slot % L.Tq;
+    bh = (slot / n) * 8 + xcd;
+    it = slot % n;
     return bh < L.B * L.H;
   }
-  const int per_xcd = (L.Tq + 7) >> 3;            // query tiles per XCD and head
+  const int per_xcd = (n + 7) >> 3;               // items per XCD and head
   bh = slot / per_xcd;
-  qt = xcd * per_xcd + (slot - bh * per_xcd);
-  return qt < L.Tq;
+  it = xcd * per_xcd + (slot - bh * per_xcd);
+  return it < n;
+}
+__device__ __forceinline__ bool work_item(const LayerDev& L, int by_heads, int& bh, int& qt) {
+  return work_item(L, L.Tq, by_heads, bh, qt);
 }
 
 template <int D, int NW, int KBK>
@@ -442,10 +449,11 @@ __global__ __launch_bounds__(64 * NW, KBK == 32 ? 4 : 2) void sparse_attn_kernel
 // that the main loop reads one LDS entry per block instead of walking the index row.
 constexpr int kTabCap = 3072;
 
+template <int KBK, int CAP>
 __device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseDev& DN,
                                                  const int32_t* idx_row, int lane, int2* tab) {
   int count = 0;
-  const int bpt = L.tile / KB;   // 1 or 2
+  const int bpt = L.tile / KBK;   // 1 or 2
   for (int s = 0; s < L.n_seg; ++s) {
     const int koff = L.seg[s].koff, K = L.seg[s].K;
     const int64_t len = L.seg[s].len, start = L.seg[s].start;
@@ -460,17 +468,17 @@ __device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseD
       int64_t rem = 0;
       if (in && lane < limit) {
         rem = len - (int64_t)t * L.tile;
-        nb = rem <= 0 ? 0 : (rem >= (int64_t)bpt * KB ? bpt : (int)((rem + KB - 1) / KB));
+        nb = rem <= 0 ? 0 : (rem >= (int64_t)bpt * KBK ? bpt : (int)((rem + KBK - 1) / KBK));
       }
       const uint64_t b1 = __builtin_amdgcn_ballot_w64(nb == 1);
       const uint64_t b2 = __builtin_amdgcn_ballot_w64(nb == 2);
       const int pre = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0)) +
                       2 * (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0));
       for (int sb = 0; sb < nb; ++sb) {
-        const int64_t r2 = rem - (int64_t)sb * KB;
+        const int64_t r2 = rem - (int64_t)sb * KBK;
         const int pos = count + pre + sb;
-        if (pos < kTabCap)
-          tab[pos] = make_int2((int)(start + (int64_t)t * L.tile + (int64_t)sb * KB), (int)(r2 < KB ? r2 : KB));
+        if (pos < CAP)
+          tab[pos] = make_int2((int)(start + (int64_t)t * L.tile + (int64_t)sb * KBK), (int)(r2 < KBK ? r2 : KBK));
       }
       count += __builtin_popcountll(b1) + 2 * __builtin_popcountll(b2);
       if (negm) break;
@@ -478,13 +486,13 @@ __device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseD
   }
   for (int r = 0; r < DN.n; ++r) {
     const int64_t len = DN.r[r].len, st = DN.r[r].start;
-    const int nbr = (int)((len + KB - 1) / KB);
+    const int nbr = (int)((len + KBK - 1) / KBK);
     for (int b0 = 0; b0 < nbr; b0 += 64) {
       const int bi = b0 + lane;
       const int pos = count + bi;
-      if (bi < nbr && pos < kTabCap) {
-        const int64_t r2 = len - (int64_t)bi * KB;
-        tab[pos] = make_int2((int)(st + (int64_t)bi * KB), (int)(r2 < KB ? r2 : KB));
+      if (bi < nbr && pos < CAP) {
+        const int64_t r2 = len - (int64_t)bi * KBK;
+        tab[pos] = make_int2((int)(st + (int64_t)bi * KBK), (int)(r2 < KBK ? r2 : KBK));
       }
     }
     count += nbr;
@@ -505,54 +513,70 @@ __device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseD
 // earlier.  The two partial results (each with its own running maximum) are merged
 // through LDS at the end.
 //
+// T2: two 64-row query tiles per workgroup.  Waves 0-1 of each group take the first
+// tile and waves 2-3 the second; each half has its own block table (half of the LDS
+// table) and its own K and V stages (half of the group's array), and blocks are 32
+// keys.  Every wave runs the slot count of the longer of the two block lists.
+//
 // K8: Q and K are FP8 (E4M3FN) codes and the first product runs on
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales); V, P and the second product stay
 // bf16.  A K row is then d bytes: the K stages use the first half of their space, a
 // block's K DMA is half as many loads, and S^T takes 2 * d / 64 products instead of d / 8.
-template <int D, bool K8>
+template <int D, bool K8, bool T2>
 __device__ __forceinline__ void pingpong_attn(
     const LayerDev& L, const DenseDev& DN, const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ q,
     const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     int by_heads) {
   using KT = std::conditional_t<K8, uint8_t, uint16_t>;
+  static_assert(!(K8 && T2), "the FP8 form runs 128-row tiles only");
   constexpr int NW = 4;                       // waves per group
-  constexpr int NT = 64 * NW;                 // threads per group
+  constexpr int KBK = T2 ? 32 : KB;           // keys per block
+  constexpr int MB = KBK / 32;                // 32-key S^T tiles per block
+  constexpr int PC = KBK / 16;                // 16-key slices of the PV contraction
+  constexpr int WS = T2 ? 2 : NW;             // waves that share one block stream (one query tile)
+  constexpr int TS = 64 * WS;                 // threads per stream
+  constexpr int CAP = T2 ? kTabCap / 2 : kTabCap;   // block-table entries per stream
   constexpr int CPR = D / 8;                  // 16-byte chunks per bf16 row
-  constexpr int SLOTS = KB * CPR;
-  constexpr int LPT = SLOTS / NT;             // V DMA loads per thread per block
+  constexpr int SLOTS = KBK * CPR;
+  constexpr int LPT = SLOTS / TS;             // V DMA loads per thread per block
   constexpr int KCPR = K8 ? D / 16 : CPR;     // 16-byte chunks per K row
-  constexpr int LPK = KB * KCPR / NT;         // K DMA loads per thread per block
-  constexpr int NPV = (D / 32) * 4;           // PV products per block
-  constexpr int NS = K8 ? 2 * (D / 64) : D / 8;   // S^T products per block
-  static_assert(SLOTS % NT == 0 && (KB * KCPR) % NT == 0 && LPK + LPT < 16, "block split");
+  constexpr int LPK = KBK * KCPR / TS;        // K DMA loads per thread per block
+  constexpr int NPV = (D / 32) * PC;          // PV products per block
+  constexpr int NS = K8 ? 2 * (D / 64) : MB * (D / 16);   // S^T products per block
+  static_assert(SLOTS % TS == 0 && (KBK * KCPR) % TS == 0 && LPK + LPT < 16, "block split");
 
   // one array per group: K stage 0, K stage 1, V stage 0, V stage 1 (the DMA is issued
   // from inline assembly, so no compiler-inserted wait depends on their aliasing)
   __shared__ __attribute__((aligned(1024))) uint16_t sg0[4 * KB * D], sg1[4 * KB * D];
   __shared__ float2 sml[NW * 64];
   __shared__ int2 stab[kTabCap];
-  __shared__ int snblk;
+  __shared__ int snblk[2];
 
   const int tid = threadIdx.x;
   const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+  const int half = T2 ? (wave >> 1) : 0;          // the stream (query tile) of this wave
+  const int wsi = T2 ? (wave & 1) : wave;         // this wave's index inside its stream
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int bh, qt;
-  if (!work_item(L, by_heads, bh, qt)) return;     // padding workgroup (uniform exit)
+  // T2: a work item is the pair of query tiles 2 it and 2 it + 1 (the second one absent
+  // for the last item of an odd tile count)
+  int bh, it;
+  if (!work_item(L, T2 ? (L.Tq + 1) >> 1 : L.Tq, by_heads, bh, it)) return;   // padding workgroup
   const int h = bh % L.H;
   const int b = bh / L.H;
+  const int qt = T2 ? 2 * it + half : it;
+  const bool tile_ok = qt < L.Tq;
 
   const int64_t q_first = L.q0 + (int64_t)qt * L.tile;
   const int64_t q_end = L.q0 + L.qlen;
   const int64_t head_off = (int64_t)b * L.sb + (int64_t)h * L.sh;
-  const int32_t* const idx_row = idx ? idx + ((int64_t)bh * L.Tq + qt) * L.Ktot : nullptr;
 
-  const int64_t my_q = q_first + wave * 32 + l32;
-  const bool q_ok = my_q < q_end;
+  const int64_t my_q = q_first + wsi * 32 + l32;
+  const bool q_ok = tile_ok && my_q < q_end;
   // Q^T operand: bf16, 8 head-dim values per product; FP8, 32 bytes per product
   // (bytes 64 ks + 32 hi .. +31 of the row, the same bytes the K operand reads)
   bf16x8 qv[K8 ? 1 : D / 16];
@@ -575,12 +599,22 @@ __device__ __forceinline__ void pingpong_attn(
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): Q is in registers before any DMA is issued
 
-  if (tid < 64) {
-    const int n = build_block_table(L, DN, idx_row, lane, stab);
-    if (lane == 0) snblk = n;
+  // wave s (s < number of streams) builds stream s's table; a stream without a tile has none
+  if (tid < (T2 ? 128 : 64)) {
+    const int st = tid >> 6;
+    const int qts = T2 ? 2 * it + st : it;
+    int n = 0;
+    if (qts < L.Tq) {
+      const int32_t* const row = idx ? idx + ((int64_t)bh * L.Tq + qts) * L.Ktot : nullptr;
+      n = build_block_table<KBK, CAP>(L, DN, row, lane, stab + st * CAP);
+    }
+    if (lane == 0) snblk[st] = n;
   }
   __syncthreads();
-  const int nblk = __builtin_amdgcn_readfirstlane(snblk);
+  const int nblk = __builtin_amdgcn_readfirstlane(snblk[half]);
+  // slots: every wave runs as many as the longer stream needs (the barriers are shared)
+  const int nmax = T2 ? __builtin_amdgcn_readfirstlane(max(snblk[0], snblk[1])) : nblk;
+  const int2* const tab = stab + half * CAP;
 
   // K row swizzle: bf16 rows (256 or 128 bytes) as in the single-pipeline kernel; FP8
   // rows (128 or 64 bytes) by row pair (quad for 64 bytes), so that the 16 rows one
@@ -589,17 +623,17 @@ __device__ __forceinline__ void pingpong_attn(
     if constexpr (K8) return (r >> (KCPR == 8 ? 1 : 2)) & (KCPR - 1);
     else return swz_k<CPR>(r);
   };
-  // load i of this thread fills 16-byte LDS slot (wave * loads + i) * 64 + lane
+  // load i of this thread fills 16-byte LDS slot (wsi * loads + i) * 64 + lane of its stream
   uint32_t koff[LPK], voff[LPT];
 #pragma unroll
   for (int i = 0; i < LPK; ++i) {
-    const int slot = (wave * LPK + i) * 64 + lane;
+    const int slot = (wsi * LPK + i) * 64 + lane;
     const int r = slot / KCPR;
     koff[i] = (uint32_t)((int64_t)r * L.sn * (int64_t)sizeof(KT) + (((slot % KCPR) ^ kswz(r)) << 4));
   }
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int slot = (wave * LPT + i) * 64 + lane;
+    const int slot = (wsi * LPT + i) * 64 + lane;
     const int r = slot / CPR;
     voff[i] = (uint32_t)((int64_t)r * L.sn * 2 + (((slot % CPR) ^ swz_v<CPR>(r)) << 4));
   }
@@ -623,8 +657,8 @@ __device__ __forceinline__ void pingpong_attn(
     constexpr int CP = IS_V ? CPR : KCPR;
     constexpr int EB = IS_V ? 2 : (int)sizeof(KT);
     const char* g = base + blk.start * L.sn * EB;
-    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t)(reinterpret_cast<char*>(dst) + wave * NL * 1024);
-    if (blk.n == KB) {
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t)(reinterpret_cast<char*>(dst) + wsi * NL * 1024);
+    if (blk.n == KBK) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         uint32_t o = off[i];
@@ -636,7 +670,7 @@ __device__ __forceinline__ void pingpong_attn(
       asm volatile("" : "+v"(ln) : : "memory");
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int r = ((wave * NL + i) * 64 + ln) / CP;
+        const int r = ((wsi * NL + i) * 64 + ln) / CP;
         const int rc = r < blk.n ? r : blk.n - 1;
         dma1(g, off[i] - (uint32_t)((r - rc) * (int)L.sn * EB), l0 + i * 1024);
       }
@@ -677,11 +711,12 @@ __device__ __forceinline__ void pingpong_attn(
   auto body = [&](auto G) {
     constexpr int GRP = decltype(G)::value;
     int j = 0;
-    uint16_t* const Gb = GRP ? sg1 : sg0;
+    // this group's stages for this wave's stream (T2: each half of the group array)
+    uint16_t* const Gb = (GRP ? sg1 : sg0) + half * 4 * KBK * D;
     uint16_t* const Ks0 = Gb;
-    uint16_t* const Ks1 = Gb + KB * D;
-    uint16_t* const Vs0 = Gb + 2 * KB * D;
-    uint16_t* const Vs1 = Gb + 3 * KB * D;
+    uint16_t* const Ks1 = Gb + KBK * D;
+    uint16_t* const Vs0 = Gb + 2 * KBK * D;
+    uint16_t* const Vs1 = Gb + 3 * KBK * D;
     // operand addresses: group base plus the lane's swizzled offset for every K column
     // step and every V column block; stage and row offsets are instruction immediates
     const uint32_t gbase = (uint32_t)(uintptr_t)(lds_void_t)Gb;
@@ -710,14 +745,14 @@ __device__ __forceinline__ void pingpong_attn(
     {
       uint4* z = reinterpret_cast<uint4*>(Vs0);
 #pragma unroll
-      for (int i = 0; i < 2 * KB * D * 2 / 16 / NT; ++i) z[i * NT + (tid & (NT - 1))] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 2 * KBK * D * 2 / 16 / TS; ++i) z[i * TS + (tid & (TS - 1))] = make_uint4(0, 0, 0, 0);
     }
 
     // this group's j-th block c_j is block 2j + GRP of the table; K(c_j) and V(c_j)
     // live in stage j % 2
     auto entry = [&](int i) {
       if (i >= nblk) return Block{0, 0};
-      const int2 e = stab[i];
+      const int2 e = tab[i];
       return Block{(int64_t)__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y)};
     };
     Block cur = entry(GRP);                   // c_j
@@ -741,80 +776,80 @@ __device__ __forceinline__ void pingpong_attn(
     // V tile the products slot issues for the other group: group 1's slot j loads group 0's
     // block j + 1, group 0's slot j (j >= 1) loads group 1's block j
     Block xo = GRP ? entry(2) : Block{0, 0};
-    uint16_t* const Go = GRP ? sg0 : sg1;
+    uint16_t* const Go = (GRP ? sg0 : sg1) + half * 4 * KBK * D;
 
-    f32x16 s[2];
-    bf16x8 pb[4];
+    f32x16 s[MB];
+    bf16x8 pb[PC];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < PC; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)0.f;
 
     typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8_t;
-    auto read_v = [&](int ST, bf16x8 (&va)[D / 32][4]) {   // V stage ST
+    auto read_v = [&](int ST, bf16x8 (&va)[D / 32][PC]) {   // V stage ST
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < PC; ++c) {
           s16x4 part[2];
 #pragma unroll
           for (int r = 0; r < 2; ++r)
             part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t)(uintptr_t)(vA[db] + (2 + ST) * KB * D * 2 + (16 * c + 8 * r) * D * 2));
+                (lds_s16x4_t)(uintptr_t)(vA[db] + (2 + ST) * KBK * D * 2 + (16 * c + 8 * r) * D * 2));
           const s16x8 both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
           va[db][c] = __builtin_bit_cast(bf16x8, both);
         }
     };
-    auto read_k = [&](int ST, auto& ka) {   // K stage ST, bf16: ka[2][D / 16]
+    auto read_k = [&](int ST, auto& ka) {   // K stage ST, bf16: ka[MB][D / 16]
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          ka[mb][kk] = *(lds_bf16x8_t)(uintptr_t)(kA[kk] + ST * KB * D * 2 + mb * 32 * D * 2);
+        for (int mb = 0; mb < MB; ++mb)
+          ka[mb][kk] = *(lds_bf16x8_t)(uintptr_t)(kA[kk] + ST * KBK * D * 2 + mb * 32 * D * 2);
     };
     typedef __attribute__((address_space(3))) const i32x4* lds_i32x4_t;
     auto read_k8 = [&](int ST, auto& ka) {  // K stage ST, FP8: ka[2][D / 64], two chunks each
 #pragma unroll
       for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const i32x4 a = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks] + ST * KB * D * 2 + mb * 32 * D);
-          const i32x4 b = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks + 1] + ST * KB * D * 2 + mb * 32 * D);
+        for (int mb = 0; mb < MB; ++mb) {
+          const i32x4 a = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks] + ST * KBK * D * 2 + mb * 32 * D);
+          const i32x4 b = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks + 1] + ST * KBK * D * 2 + mb * 32 * D);
           ka[mb][ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    auto mul_pv = [&](const bf16x8 (&va)[D / 32][4]) {
+    auto mul_pv = [&](const bf16x8 (&va)[D / 32][PC]) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < PC; ++c)
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[c], o[db], 0, 0, 0);
     };
     auto mul_s = [&](const auto& ka) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mb][kk], qv[kk], s[mb], 0, 0, 0);
     };
     // FP8 E4M3 operands (format code 0 for A and B), unit block scales (E8M0 code 127)
     auto mul_s8 = [&](const auto& ka) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
           s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[mb][ks], qv8[ks], s[mb], 0, 0, 0, 127, 0, 127);
     };
 
@@ -824,7 +859,7 @@ __device__ __forceinline__ void pingpong_attn(
     // Operand reads run four products ahead; no VALU instruction is left in this slot.
     auto mphase = [&](auto stage) {
       constexpr int ST = decltype(stage)::value;
-      bf16x8 va[D / 32][4];
+      bf16x8 va[D / 32][PC];
       read_v(1 - ST, va);
       // V reads (2 per PV product), then K reads; 8 reads go first, then each PV
       // product is followed by two reads, the last four by one
@@ -848,7 +883,7 @@ __device__ __forceinline__ void pingpong_attn(
         if constexpr (NKR > 4) __builtin_amdgcn_sched_group_barrier(0x100, NKR - 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
       } else {
-        bf16x8 ka[2][D / 16];
+        bf16x8 ka[MB][D / 16];
         read_k(ST, ka);
         mul_pv(va);
         mul_s(ka);
@@ -874,7 +909,7 @@ __device__ __forceinline__ void pingpong_attn(
       int nc = 0;
       if (xo.n > 0) {
         // group 1 fills group 0's V stage (j+1)%2, group 0 fills group 1's V stage j%2
-        dma(kV, vbase, voff, xo, Go + (2 + (GRP ? 1 - ST : ST)) * KB * D);
+        dma(kV, vbase, voff, xo, Go + (2 + (GRP ? 1 - ST : ST)) * KBK * D);
         nc = LPT;
       }
       wait_vm(nc + np);                       // loads of two phases ago have landed
@@ -888,9 +923,9 @@ __device__ __forceinline__ void pingpong_attn(
       constexpr int ST = decltype(stage)::value;
       uint16_t* Kf = ST ? Ks1 : Ks0;
       const int i3 = 2 * (j + 3) + GRP;
-      const int2 e3 = i3 < nblk ? stab[i3] : make_int2(0, 0);
+      const int2 e3 = i3 < nblk ? tab[i3] : make_int2(0, 0);
       const int io = GRP ? 2 * (j + 2) : 2 * (j + 1) + 1;
-      const int2 eo = io < nblk ? stab[io] : make_int2(0, 0);
+      const int2 eo = io < nblk ? tab[io] : make_int2(0, 0);
       int nc = 0;
       if (nx2.n > 0) {
         dma(kK, kbase, koff, nx2, Kf);
@@ -898,12 +933,12 @@ __device__ __forceinline__ void pingpong_attn(
       }
       if (cur.n > 0) {
         const int n = cur.n;
-        if (n < KB) {
+        if (n < KBK) {
           int kb = hi * 4;
           float ninf = -INFINITY;
           asm volatile("" : "+v"(kb), "+v"(ninf) : : "memory");
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const int c = mb * 32 + (e >> 2) * 8 + (e & 3);
@@ -913,13 +948,13 @@ __device__ __forceinline__ void pingpong_attn(
         // weights against the running maximum as it stands, and this lane's sum of them
         auto weights = [&]() {
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
               pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
           float bs = 0.f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < PC; ++c) {
             const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
             const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
             bs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, bs, false);
@@ -930,13 +965,13 @@ __device__ __forceinline__ void pingpong_attn(
           return bs;
         };
         float bs = weights();
-        // Weights are kept while no lane's 32 of them sum above kLazySum (none
-        // exceeds it then).  Otherwise (the first block: m_run = -inf gives inf or NaN)
+        // Weights are kept while no lane's weights (16 per 32 keys) sum above kLazySum
+        // (none exceeds it then).  Otherwise (the first block: m_run = -inf gives inf or NaN)
         // the running maximum moves to this block's maximum and the weights are redone.
         if (__builtin_amdgcn_ballot_w64(!(bs <= kLazySum)) != 0) {
           float mx = -INFINITY;
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -955,7 +990,7 @@ __device__ __forceinline__ void pingpong_attn(
       } else {
         // no block: the next PV adds zero
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < PC; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)0.f;
       }
@@ -971,8 +1006,8 @@ __device__ __forceinline__ void pingpong_attn(
       nx2 = nx3;
       ++j;
     };
-    // slots: ceil(nblk / 2) + 1 products/softmax pairs, the same count in both groups
-    const int iters = nblk > 0 ? (nblk + 1) / 2 + 1 : 0;
+    // slots: ceil(nmax / 2) + 1 products/softmax pairs, the same count in every wave
+    const int iters = nmax > 0 ? (nmax + 1) / 2 + 1 : 0;
     while (j < iters) {
       mphase(std::integral_constant<int, 0>{});
       vphase(std::integral_constant<int, 0>{});
@@ -1051,7 +1086,17 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
-  pingpong_attn<D, false>(L, DN, q, k, v, idx, scale_log2, out, lse, by_heads);
+  pingpong_attn<D, false, false>(L, DN, q, k, v, idx, scale_log2, out, lse, by_heads);
+}
+
+// 64-row tiles: one workgroup takes two neighbouring query tiles, waves 0-1 and 2-3 of each
+// group one tile each, with 32-key blocks (each tile's own block stream and table).
+template <int D>
+__global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_pair_kernel(
+    LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, false, true>(L, DN, q, k, v, idx, scale_log2, out, lse, by_heads);
 }
 
 // Q and K as FP8 codes with per-tensor scales (device floats): logits are
@@ -1062,49 +1107,70 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_fp8qk_pingpong_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale, uint16_t* __restrict__ out,
     float* __restrict__ lse, int by_heads) {
-  pingpong_attn<D, true>(L, DN, q, k, v, idx, scale_log2 * q_scale[0] * k_scale[0], out, lse, by_heads);
+  pingpong_attn<D, true, false>(L, DN, q, k, v, idx, scale_log2 * q_scale[0] * k_scale[0], out, lse, by_heads);
 }
 
 }  // namespace
 
 // 128-row tiles take the two-group kernel when the row's block list fits its LDS table
 // and every token index fits the table's 32-bit entries
-bool two_group_fits(const LayerDev& L, const DenseDev& DN) {
-  int64_t bound = (int64_t)L.Ktot * (L.tile / KB);
+namespace {
+// the block list of one query tile fits a two-group table of cap entries of kbk keys, and
+// every token index fits the table's 32-bit entries
+bool table_fits(const LayerDev& L, const DenseDev& DN, int kbk, int64_t cap) {
+  int64_t bound = (int64_t)L.Ktot * (L.tile / kbk);
   int64_t last = 0;
   for (int i = 0; i < DN.n; ++i) {
-    bound += (DN.r[i].len + KB - 1) / KB;
+    bound += (DN.r[i].len + kbk - 1) / kbk;
     last = DN.r[i].start + DN.r[i].len > last ? DN.r[i].start + DN.r[i].len : last;
   }
   for (int i = 0; i < L.n_seg; ++i)
     last = L.seg[i].start + L.seg[i].len > last ? L.seg[i].start + L.seg[i].len : last;
-  return L.tile == 128 && bound <= kTabCap && last < ((int64_t)1 << 31);
+  return bound <= cap && last < ((int64_t)1 << 31);
 }
 
-namespace {
-bool grid_of(const LayerDev& L, const int32_t* idx, dim3& grid, int& by_heads) {
+// grid of n work items per (b, h), in work_item's XCD-aware order
+bool grid_of(const LayerDev& L, int64_t n, const int32_t* idx, dim3& grid, int& by_heads) {
   by_heads = idx == nullptr && L.B * L.H >= 8;
-  const int64_t per_xcd = (L.Tq + 7) / 8;
-  const int64_t nwork = by_heads ? ((int64_t)L.B * L.H + 7) / 8 * 8 * L.Tq : (int64_t)L.B * L.H * per_xcd * 8;
+  const int64_t per_xcd = (n + 7) / 8;
+  const int64_t nwork = by_heads ? ((int64_t)L.B * L.H + 7) / 8 * 8 * n : (int64_t)L.B * L.H * per_xcd * 8;
   if (nwork > 0x7FFFFFFF) return false;
   grid = dim3((unsigned)nwork);
   return true;
 }
 }  // namespace
 
+// 128-row tiles take the two-group kernel when the row's block list fits its LDS table
+bool two_group_fits(const LayerDev& L, const DenseDev& DN) {
+  return L.tile == 128 && table_fits(L, DN, KB, kTabCap);
+}
+
+// 64-row tiles take the paired two-group kernel when each tile's list of 32-key blocks
+// fits half the table
+bool pair_fits(const LayerDev& L, const DenseDev& DN) {
+  return L.tile == 64 && table_fits(L, DN, 32, kTabCap / 2);
+}
+
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void* q, const void* k,
                               const void* v, const int32_t* idx, float scale, void* out, float* lse,
                               hipStream_t s) {
+  const bool two_group = two_group_fits(L, DN);
+  const bool pair = pair_fits(L, DN);
   dim3 grid;
   int by_heads;
-  if (!grid_of(L, idx, grid, by_heads)) return hipErrorInvalidValue;
+  if (!grid_of(L, pair ? ((int64_t)L.Tq + 1) / 2 : L.Tq, idx, grid, by_heads)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(out);
-  const bool two_group = two_group_fits(L, DN);
-  if (two_group && L.d == 128)
+  if (pair && L.d == 128)
+    hipLaunchKernelGGL((sparse_attn_pingpong_pair_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
+                       scale_log2, oo, lse, by_heads);
+  else if (pair)
+    hipLaunchKernelGGL((sparse_attn_pingpong_pair_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
+                       scale_log2, oo, lse, by_heads);
+  else if (two_group && L.d == 128)
     hipLaunchKernelGGL((sparse_attn_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
   else if (two_group)
@@ -1130,7 +1196,7 @@ hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& DN, const
                                     const float* k_scale, void* out, float* lse, hipStream_t s) {
   dim3 grid;
   int by_heads;
-  if (!grid_of(L, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
+  if (!grid_of(L, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
   auto qq = static_cast<const uint8_t*>(q8);
   auto kk = static_cast<const uint8_t*>(k8);

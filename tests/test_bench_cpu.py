@@ -29,4 +29,5 @@ def test_attention_kernel_name_follows_the_launcher_rule():
     b = _bench()
     names = {n: b.attention_kernel_name(wl) for n, wl in I.WORKLOADS.items()}
     assert names["t2v5s"] == names["r2va"] == names["t2v14s"] == "sparse_attn_pingpong_kernel<128>"
-    assert names["mid"] == "sparse_attn_kernel<128, 2, 32>" and names["tiny"] == "sparse_attn_kernel<64, 2, 32>"
+    assert names["mid"] == "sparse_attn_pingpong_pair_kernel<128>"
+    assert names["tiny"] == "sparse_attn_pingpong_pair_kernel<64>"
