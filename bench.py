@@ -208,11 +208,25 @@ def device_peaks(log):
 
 
 def environment():
+    """Device, software versions and the GPU clock levels rocm-smi reports once the timed work is
+    over (the idle levels; the clock under sustained MFMA load is not sampled here)."""
     import platform
+    import subprocess
     import torch
     p = torch.cuda.get_device_properties(0)
-    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
-            "hip": torch.version.hip, "torch": torch.__version__, "host": platform.node()}
+    env = {"device": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+           "hip": torch.version.hip, "torch": torch.__version__, "host": platform.node()}
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        env["clocks_after_run"] = [ln.split(":", 1)[1].strip() for ln in r.stdout.splitlines()
+                                   if "clk" in ln.lower() and "level" in ln.lower()]
+    except (OSError, subprocess.SubprocessError):
+        env["clocks_after_run"] = None
+    return env
 
 
 def copy_calibration():
