@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 
 #include "common.h"
@@ -13,7 +14,8 @@ namespace {
 
 using veda::LayerDev;
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (a may be close to INT64_MAX)
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -30,6 +32,8 @@ bool overlap(const veda_range& a, const veda_range& b) {
 int check_layer(const veda_layer* L, bool for_select) {
   if (!L) return VEDA_EINVAL;
   if (L->B < 1 || L->H < 1 || L->n_tokens < 1) return VEDA_EINVAL;
+  // B * H is an int32 on the device
+  if ((int64_t)L->B * L->H > INT32_MAX) return VEDA_EUNSUPPORTED;
   if (L->d != 64 && L->d != 128) return VEDA_EUNSUPPORTED;
   if (L->tile != 64 && L->tile != 128) return VEDA_EUNSUPPORTED;
   if (for_select && (L->p < 16 || L->p > 384 || (L->p % 16) != 0)) return VEDA_EUNSUPPORTED;
@@ -53,10 +57,12 @@ int check_layer(const veda_layer* L, bool for_select) {
     tk += ceil_div(L->seg[s].len, L->tile);
   }
   if (for_select && tk > VEDA_MAX_KEY_TILES) return VEDA_EUNSUPPORTED;
-  // index offsets are int32 inside the kernels
-  if ((int64_t)L->B * L->H * ceil_div(L->query.len, L->tile) * std::max<int64_t>(tk, 1) >
-      (int64_t)1 << 40)
-    return VEDA_EUNSUPPORTED;
+  // tile counts are int32 on the device
+  const int64_t tq = ceil_div(L->query.len, L->tile);
+  if (tq > INT32_MAX || tk > INT32_MAX) return VEDA_EUNSUPPORTED;
+  // index and mass rows: B * H * Tq * sum T_s entries at most 2^40, so that every offset
+  // formed from them on the device stays far inside int64
+  if ((__int128)L->B * L->H * tq * std::max<int64_t>(tk, 1) > (__int128)1 << 40) return VEDA_EUNSUPPORTED;
   return VEDA_OK;
 }
 
@@ -129,6 +135,8 @@ const char* veda_status_string(int status) {
 
 int64_t veda_k_total(const veda_layer* layer) {
   if (!layer || layer->tile <= 0 || layer->n_seg < 0 || layer->n_seg > VEDA_MAX_SEGMENTS) return -1;
+  for (int s = 0; s < layer->n_seg; ++s)
+    if (layer->seg[s].len < 0 || layer->budget[s] < 0) return -1;
   return k_total(layer);
 }
 

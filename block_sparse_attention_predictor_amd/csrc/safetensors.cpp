@@ -134,6 +134,8 @@ struct Json {
             cp = 0x10000 + ((cp - 0xD800) << 10) + (lo - 0xDC00);
           } else if (cp >= 0xDC00 && cp < 0xE000) {
             return false;
+          } else if (cp == 0) {   // names and metadata are handed out as C strings
+            return false;
           }
           put_utf8(out, cp);
           break;
@@ -328,7 +330,7 @@ int veda_st_open(const char* path, veda_st_file** out) {
 
 void veda_st_close(veda_st_file* f) { delete f; }
 
-int64_t veda_st_count(const veda_st_file* f) { return f ? (int64_t)f->tensors.size() : VEDA_EINVAL; }
+int64_t veda_st_count(const veda_st_file* f) { return f ? (int64_t)f->tensors.size() : (int64_t)VEDA_EINVAL; }
 
 int veda_st_info(const veda_st_file* f, int64_t i, const char** name, int32_t* dtype, int32_t* ndim,
                  int64_t* shape, int64_t* nbytes) {
@@ -359,7 +361,7 @@ int veda_st_read(const veda_st_file* f, int64_t i, void* dst, int64_t nbytes) {
 }
 
 int64_t veda_st_metadata_count(const veda_st_file* f) {
-  return f ? (int64_t)f->meta.size() : VEDA_EINVAL;
+  return f ? (int64_t)f->meta.size() : (int64_t)VEDA_EINVAL;
 }
 
 int veda_st_metadata_at(const veda_st_file* f, int64_t i, const char** key, const char** value) {

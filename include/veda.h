@@ -49,7 +49,9 @@ typedef enum veda_status {
   VEDA_EINVAL = -1,        /* null pointer, non-positive size, misaligned pointer or stride */
   VEDA_EUNSUPPORTED = -2,  /* d not in {64,128}, tile not in {64,128}, p not a multiple of 16
                               in [16, 384], more than VEDA_MAX_SEGMENTS / VEDA_MAX_DENSE,
-                              more than VEDA_MAX_KEY_TILES key tiles, stride_n >= 2^24 */
+                              more than VEDA_MAX_KEY_TILES key tiles, stride_n >= 2^24;
+                              size limits: B*H, Tq and sum_s T_s at most 2^31 - 1, and
+                              B*H*Tq*max(1, sum_s T_s) at most 2^40 */
   VEDA_EWORKSPACE = -3,    /* workspace smaller than veda_select_workspace_bytes() */
   VEDA_ERANGE = -4,        /* a range leaves [0, n_tokens), key segments overlap each other,
                               or a dense range overlaps a key segment or another dense range */
@@ -336,7 +338,8 @@ int veda_mfma_peak(float* out, int32_t iters, int32_t workgroups, void* stream);
  * then the data.  veda_st_open checks the whole header (offsets inside the file,
  * byte counts = dtype size x shape, the tensors tiling the data without holes or
  * overlap) and returns VEDA_EIO (cannot open/read) or VEDA_EFORMAT (malformed).
- * Names, metadata strings and the handle stay valid until veda_st_close.  Tensors
+ * A string holding U+0000 is rejected (VEDA_EFORMAT): names and metadata come back
+ * as C strings.  Names, metadata strings and the handle stay valid until veda_st_close.  Tensors
  * keep the file's order.  veda_st_read copies a tensor's raw little-endian bytes into
  * host memory of exactly veda_st_info's nbytes.
  */

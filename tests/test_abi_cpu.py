@@ -95,6 +95,36 @@ def test_range_errors():
     assert check(L, for_select=False) == 0
 
 
+def _one_segment(n_q, n_k, tile=64, B=1, H=1):
+    n = max(n_q, n_k) + 64
+    return Bnd.make_layer(B=B, H=H, d=64, p=16, tile=tile, n_tokens=n, query=(0, n_q),
+                          segments=[(0, n_k, 1)], strides=(0, H * 64, 64))
+
+
+def test_size_limits():
+    """Counts the kernels hold in 32 bits and the 2^40 index volume, each at its boundary;
+    sizes near INT64_MAX are rejected, not overflowed."""
+    big = (1 << 63) - 1
+    # query tiles: 2^31 - 1 is accepted, 2^31 is not
+    assert check(_one_segment((2**31 - 1) * 64, 64), for_select=False) == 0
+    assert check(_one_segment(2**31 * 64, 64), for_select=False) == -2
+    # B * H
+    assert check(_one_segment(64, 64, B=2**16, H=2**15 - 1), for_select=False) == 0
+    assert check(_one_segment(64, 64, B=2**16, H=2**15), for_select=False) == -2
+    # B * H * Tq * sum T_s: 2^40 exactly, then one key tile more
+    assert check(_one_segment(2**26, 2**26), for_select=False) == 0
+    assert check(_one_segment(2**26, 2**26 + 1), for_select=False) == -2
+    # lengths near INT64_MAX
+    L = Bnd.make_layer(B=1, H=1, d=64, p=16, tile=128, n_tokens=big, query=(0, big),
+                       segments=[(0, big, 4)], strides=(0, 64, 64))
+    assert check(L) == -2 and check(L, for_select=False) == -2
+    assert Bnd.select_workspace_bytes(L) == 0
+    lib = Bnd._load()
+    assert lib.veda_k_total(ctypes.byref(L)) == 4
+    L.seg[0].len = -1
+    assert lib.veda_k_total(ctypes.byref(L)) == -1
+
+
 def test_entry_points_reject_before_device_calls():
     lib = Bnd._load()
     L = _layer()

@@ -125,6 +125,9 @@ def test_malformed_files(tmp_path):
         "lone_surrogate": (b'{"x\\udc00": {"dtype": "F32", "shape": [2], "data_offsets": [0, 8]}}',
                            d8, None),
         "not_object": (b'["x"]', b"", None),
+        # U+0000 cannot come back through a C string
+        "nul_in_name": ({"x\u0000y": t}, d8, None),
+        "nul_in_metadata": ({"__metadata__": {"k": "a\u0000"}, "x": t}, d8, None),
     }
     for name, spec in cases.items():
         path = tmp_path / f"{name}.safetensors"
