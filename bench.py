@@ -31,7 +31,7 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -50,7 +50,22 @@ def parse():
                     help="skip the FP8 Q.K^T path timing (field 'fp8qk')")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (byte-counter calibration)")
-    return ap.parse_args()
+    ap.add_argument("--record", default=None, metavar="FILE",
+                    help="also append the JSON line, with a UTC time stamp, to FILE (JSON Lines, one record "
+                         "per run; existing records are never rewritten)")
+    return ap.parse_args(argv)
+
+
+def append_record(path: str, line: dict) -> None:
+    """Append one run's record to a JSON Lines file, as a single write of one line."""
+    rec = dict(line)
+    rec["recorded_at"] = time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())
+    data = (json.dumps(rec) + "\n").encode()
+    fd = os.open(path, os.O_WRONLY | os.O_APPEND | os.O_CREAT, 0o644)
+    try:
+        os.write(fd, data)
+    finally:
+        os.close(fd)
 
 
 def attended_tokens_per_tile(wl, idx: np.ndarray, widths=None) -> np.ndarray:
@@ -689,6 +704,8 @@ def main():
         "detail": res,
     }
     print(json.dumps(line))
+    if args.record:
+        append_record(args.record, line)
 
 
 if __name__ == "__main__":

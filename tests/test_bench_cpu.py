@@ -31,3 +31,17 @@ def test_attention_kernel_name_follows_the_launcher_rule():
     assert names["t2v5s"] == names["r2va"] == names["t2v14s"] == "sparse_attn_pingpong_kernel<128>"
     assert names["mid"] == "sparse_attn_pingpong_pair_kernel<128>"
     assert names["tiny"] == "sparse_attn_pingpong_pair_kernel<64>"
+
+
+def test_record_appends_one_json_line_per_run(tmp_path):
+    b = _bench()
+    p = str(tmp_path / "runs.jsonl")
+    assert b.parse(["--record", p]).record == p and b.parse([]).record is None
+    b.append_record(p, {"metric": "m", "value": 1.0})
+    first = open(p).read()
+    b.append_record(p, {"metric": "m", "value": 2.0})
+    text = open(p).read()
+    assert text.startswith(first)                      # earlier records are left as they were
+    recs = [json.loads(x) for x in text.splitlines()]
+    assert [r["value"] for r in recs] == [1.0, 2.0]
+    assert all(r["recorded_at"].endswith("Z") for r in recs)
