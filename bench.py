@@ -230,7 +230,8 @@ def environment():
     import torch
     p = torch.cuda.get_device_properties(0)
     env = {"device": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
-           "hip": torch.version.hip, "torch": torch.__version__, "host": platform.node()}
+           "hip": torch.version.hip, "torch": torch.__version__, "host": platform.node(),
+           "host_cpus": len(os.sched_getaffinity(0))}
     try:
         env["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:
