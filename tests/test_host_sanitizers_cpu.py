@@ -1,7 +1,8 @@
 """The host code of the C ABI under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 csrc/api.cpp (the argument validation of every entry point) and csrc/safetensors.cpp (the
-file reader) are built with g++ -fsanitize=address,undefined, host code only, and linked
+file reader) are built with g++ -fsanitize=address,undefined (and the standard library's
+own bounds assertions), host code only, and linked
 with tests/c/launch_stubs.cpp in place of the kernel launchers, so no device is involved.
 tests/c/host_fuzz.cpp then drives them with random and extreme layer descriptions (sizes
 near the int32 and int64 limits, overlapping and out-of-range token ranges, null and
@@ -33,7 +34,7 @@ def fuzz_exe(tmp_path_factory):
     sources = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "safetensors.cpp"),
                os.path.join(ROOT, "tests", "c", "launch_stubs.cpp"), os.path.join(ROOT, "tests", "c", "host_fuzz.cpp")]
     flags = ["-std=c++17", "-O1", "-g", "-Wall", "-Wextra", "-Werror", "-fno-omit-frame-pointer",
-             "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-D_GLIBCXX_ASSERTIONS", "-D__HIP_PLATFORM_AMD__",
              "-I", os.path.join(ROOT, "include"), "-isystem", os.path.join(ROCM, "include")]
     r = subprocess.run(["g++", *flags, *sources, "-o", exe], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-4000:]
