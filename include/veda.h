@@ -92,7 +92,9 @@ typedef struct veda_layer {
   int32_t reserved;   /* must be 0                                                */
 } veda_layer;
 
-/* Ktot = sum_s min(budget[s], T_s): index entries per (b, h, query tile). */
+/* Ktot = sum_s min(budget[s], T_s): index entries per (b, h, query tile).  -1 for a null
+ * layer, tile <= 0, n_seg outside [0, VEDA_MAX_SEGMENTS], or a negative segment length or
+ * budget.  No other check is made (veda_layer_check does those). */
 int64_t veda_k_total(const veda_layer* layer);
 
 /* Library ABI version (VEDA_ABI_VERSION of the build). */
