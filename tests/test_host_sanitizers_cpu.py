@@ -56,3 +56,50 @@ def test_host_code_under_sanitizers(fuzz_exe, tmp_path, seed):
     assert m and int(m[1]) > 300 and int(m[2]) > 10, r.stdout
     m = re.search(r"checks: (\d+)", r.stdout)
     assert m and int(m[1]) > 1000000, r.stdout
+
+
+# Plausible mistakes, each re-inserted into a temporary copy of one host source: the fuzzer
+# must fail on every one of them (a sanitizer report, a launch stand-in's precondition or
+# one of its own properties).
+MUTATIONS = {
+    "ceil_div_overflows": ("api.cpp", "int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }",
+                           "int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }"),
+    "missing_index_check": ("api.cpp", "  if (!idx && D.Ktot != D.Tk) return VEDA_EINVAL;", ""),
+    "dense_overlap_unchecked": ("api.cpp", "      if (overlap(dense[i], dense[j])) return VEDA_ERANGE;", "      ;"),
+    "nul_accepted": ("safetensors.cpp", "          } else if (cp == 0) {", "          } else if (cp == 0xFFFFFFFF) {"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_fuzzer_catches_planted_mistakes(tmp_path, name):
+    fname, old, new = MUTATIONS[name]
+    sources = {f: open(os.path.join(CSRC, f)).read() for f in ("api.cpp", "safetensors.cpp", "common.h")}
+    assert sources[fname].count(old) == 1, "mutation site not found"
+    sources[fname] = sources[fname].replace(old, new)
+    # the copies keep their relative includes: <tmp>/pkg/csrc/*.cpp -> <tmp>/include/veda.h
+    csrc = tmp_path / "pkg" / "csrc"
+    csrc.mkdir(parents=True)
+    for f, text in sources.items():
+        (csrc / f).write_text(text)
+    (tmp_path / "include").mkdir()
+    (tmp_path / "include" / "veda.h").write_text(open(os.path.join(ROOT, "include", "veda.h")).read())
+    exe = str(tmp_path / "host_fuzz")
+    flags = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I", str(tmp_path / "include"),
+             "-isystem", os.path.join(ROCM, "include")]
+    stubs = [os.path.join(ROOT, "tests", "c", "launch_stubs.cpp"), os.path.join(ROOT, "tests", "c", "host_fuzz.cpp")]
+    # the stand-ins include common.h by a path relative to tests/c; point them at the copy
+    for s in stubs:
+        text = open(s).read().replace("../../block_sparse_attention_predictor_amd/csrc/common.h",
+                                      str(csrc / "common.h")).replace("../../include/veda.h",
+                                                                      str(tmp_path / "include" / "veda.h"))
+        (tmp_path / os.path.basename(s)).write_text(text)
+    shutil.copy(os.path.join(ROOT, "tests", "c", "launch_stubs.h"), tmp_path / "launch_stubs.h")
+    r = subprocess.run(["g++", *flags, str(csrc / "api.cpp"), str(csrc / "safetensors.cpp"),
+                        str(tmp_path / "launch_stubs.cpp"), str(tmp_path / "host_fuzz.cpp"), "-o", exe],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    files = tmp_path / "files"
+    files.mkdir()
+    r = subprocess.run([exe, str(files), "1", "40000", "50"], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "the planted mistake went unnoticed:\n" + r.stdout[-2000:]
