@@ -50,10 +50,23 @@ def parse(argv=None):
                     help="skip the FP8 Q.K^T path timing (field 'fp8qk')")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (byte-counter calibration)")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="input seed for every workload (default: each workload's own index)")
     ap.add_argument("--record", default=None, metavar="FILE",
                     help="also append the JSON line, with a UTC time stamp, to FILE (JSON Lines, one record "
                          "per run; existing records are never rewritten)")
     return ap.parse_args(argv)
+
+
+SEED = None   # --seed: replaces every workload's input seed
+
+
+def workload(name):
+    """The named workload, with its input seed replaced when --seed is given."""
+    import dataclasses
+    from block_sparse_attention_predictor_amd import inputs as I
+    wl = I.WORKLOADS[name]
+    return wl if SEED is None else dataclasses.replace(wl, index=SEED)
 
 
 def append_record(path: str, line: dict) -> None:
@@ -100,7 +113,7 @@ class Layer:
         from block_sparse_attention_predictor_amd import inputs as I
         self.B = B
         self.I = I
-        self.wl = wl = I.WORKLOADS[name]
+        self.wl = wl = workload(name)
         self.q, self.k, self.v = I.make_qkv(wl)
         self.w = I.make_weights(wl)
         dev = torch.device("cuda:0")
@@ -600,7 +613,9 @@ def recorded_traffic(workload):
 
 
 def main():
+    global SEED
     args = parse()
+    SEED = args.seed
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the path is built and "
                                    "measured on one GPU's share of a layer and is not sharded across GPUs"}))
@@ -669,7 +684,7 @@ def main():
         "config": {"workload": args.workload, "B": wl.B, "H": wl.H, "d": wl.d, "p": wl.p,
                    "tile": wl.tile, "n_tokens": wl.n_tokens, "query_tokens": wl.query.length,
                    "budgets": {s.name: s.budget for s in wl.segments},
-                   "dense_tokens": sum(r.length for r in wl.dense)},
+                   "dense_tokens": sum(r.length for r in wl.dense), "seed": wl.index},
         "selector_ms": round(res["selector_ms"], 4),
         "full_layer_ms": round(res["full_layer_ms"], 4),
         "attn_ms": round(res["attn_ms"], 4),

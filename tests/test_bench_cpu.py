@@ -45,3 +45,19 @@ def test_record_appends_one_json_line_per_run(tmp_path):
     recs = [json.loads(x) for x in text.splitlines()]
     assert [r["value"] for r in recs] == [1.0, 2.0]
     assert all(r["recorded_at"].endswith("Z") for r in recs)
+
+
+def test_seed_replaces_every_workloads_input_seed():
+    import numpy as np
+    b = _bench()
+    assert b.parse(["--seed", "7"]).seed == 7 and b.parse([]).seed is None
+    base = b.workload("tiny")
+    b.SEED = 7
+    try:
+        w7 = b.workload("tiny")
+    finally:
+        b.SEED = None
+    assert w7.index == 7 != base.index
+    assert (w7.n_tokens, w7.segments, w7.dense) == (base.n_tokens, base.segments, base.dense)
+    q0, q7 = I.make_qkv(base)[0], I.make_qkv(w7)[0]
+    assert q0.shape == q7.shape and not np.array_equal(q0, q7)
