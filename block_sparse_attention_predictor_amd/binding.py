@@ -86,6 +86,7 @@ def _load():
         "veda_pool_project": (ctypes.c_int, [L, P, P, P, P, P, P, P]),
         "veda_score_topk": (ctypes.c_int, [L, P, P, P, P, P]),
         "veda_select": (ctypes.c_int, [L, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "veda_select_noalloc": (ctypes.c_int, [L, P, P, P, P, P, P, P]),
         "veda_sparse_attn": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                             ctypes.c_float, P, P, P]),
         "veda_dequant_fp8_e4m3": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
@@ -128,7 +129,7 @@ def _load():
 def exported_symbols():
     return [n for n in ("veda_abi_version", "veda_status_string", "veda_k_total", "veda_layer_check",
                         "veda_select_workspace_bytes", "veda_pool_project", "veda_score_topk",
-                        "veda_select", "veda_sparse_attn", "veda_dequant_fp8_e4m3",
+                        "veda_select", "veda_select_noalloc", "veda_sparse_attn", "veda_dequant_fp8_e4m3",
                         "veda_sparse_attn_check", "veda_layer_attn", "veda_window_width",
                         "veda_window_indices", "veda_block_mass", "veda_block_recall",
                         "veda_st_open", "veda_st_close", "veda_st_count", "veda_st_info",
@@ -228,6 +229,28 @@ def _check_w(layer: Layer, *ws):
                              "(layer.wdtype selects float16 or bfloat16)")
 
 
+def _check_idx(layer: Layer, idx, device, ktot=None):
+    """idx must be a contiguous int32 [B, H, Tq, Ktot] tensor on `device` (the kernels read
+    and write it with the layer's geometry and cannot detect a smaller buffer)."""
+    ktot = layer.Ktot if ktot is None else ktot
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or \
+            tuple(idx.shape) != (layer.B, layer.H, layer.Tq, ktot):
+        raise ValueError(f"idx must be contiguous int32 [B, H, Tq, Ktot] = "
+                         f"{[layer.B, layer.H, layer.Tq, ktot]}")
+    if idx.device != device:
+        raise ValueError(f"idx is on {idx.device}, expected {device}")
+
+
+def _check_hat(layer: Layer, x, rows: int, device, what: str):
+    """q_hat / k_hat: contiguous fp32 [B, H, rows, p] on `device`."""
+    if x.dtype != torch.float32 or not x.is_contiguous() or \
+            tuple(x.shape) != (layer.B, layer.H, rows, layer.p):
+        raise ValueError(f"{what} must be contiguous fp32 [B, H, {rows}, p] = "
+                         f"{[layer.B, layer.H, rows, layer.p]}")
+    if x.device != device:
+        raise ValueError(f"{what} is on {x.device}, expected {device}")
+
+
 def select_workspace_bytes(layer: Layer) -> int:
     return _load().veda_select_workspace_bytes(ctypes.byref(layer))
 
@@ -247,6 +270,10 @@ def project(layer: Layer, q, k, wq, wk, stream=None):
 
 def score_topk(layer: Layer, q_hat, k_hat, want_scores: bool = False, stream=None):
     dev = q_hat.device
+    if not q_hat.is_cuda:
+        raise ValueError("q_hat must be a device tensor")
+    _check_hat(layer, q_hat, layer.Tq, dev, "q_hat")
+    _check_hat(layer, k_hat, layer.Tk, dev, "k_hat")
     idx = torch.empty((layer.B, layer.H, layer.Tq, layer.Ktot), dtype=torch.int32, device=dev)
     sc = torch.empty((layer.B, layer.H, layer.Tq, layer.Tk), dtype=torch.float32, device=dev) \
         if want_scores else None
@@ -264,6 +291,8 @@ def select(layer: Layer, q, k, wq, wk, want_scores: bool = False, workspace=None
     dev = q.device
     if idx is None:
         idx = torch.empty((layer.B, layer.H, layer.Tq, layer.Ktot), dtype=torch.int32, device=dev)
+    else:
+        _check_idx(layer, idx, dev)
     sc = torch.empty((layer.B, layer.H, layer.Tq, layer.Tk), dtype=torch.float32, device=dev) \
         if want_scores else None
     nbytes = select_workspace_bytes(layer)
@@ -277,6 +306,25 @@ def select(layer: Layer, q, k, wq, wk, want_scores: bool = False, workspace=None
     return (idx, sc) if want_scores else idx
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20   # VEDA_NOALLOC_SCRATCH_BYTES
+
+
+def select_noalloc(layer: Layer, q, k, wq, wk, idx, scores=None, stream=None):
+    """veda_select_noalloc: selection into caller-supplied idx (and optional scores) with the
+    workspace in the library's own per-GPU array; nothing is allocated by this call."""
+    _check_qkv(layer, q, k)
+    _check_w(layer, wq, wk)
+    _check_idx(layer, idx, q.device)
+    if scores is not None and (scores.dtype != torch.float32 or not scores.is_contiguous() or
+                               tuple(scores.shape) != (layer.B, layer.H, layer.Tq, layer.Tk) or
+                               scores.device != q.device):
+        raise ValueError("scores must be contiguous fp32 [B, H, Tq, Tk] on q's device")
+    st = _load().veda_select_noalloc(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(idx),
+                                     _ptr(scores), _stream(stream))
+    _check(st, "veda_select_noalloc")
+    return idx
+
+
 def sparse_attn(layer: Layer, q, k, v, idx, dense: Sequence[Tuple[int, int]] = (),
                 scale: float = 0.0, out=None, want_lse: bool = False, stream=None):
     """Block-sparse attention; returns out (bf16, q's shape) [and lse fp32 [B, H, query.len]]."""
@@ -288,9 +336,7 @@ def sparse_attn(layer: Layer, q, k, v, idx, dense: Sequence[Tuple[int, int]] = (
     lse = torch.empty((layer.B, layer.H, layer.query.len), dtype=torch.float32, device=q.device) \
         if want_lse else None
     if idx is not None:
-        if idx.dtype != torch.int32 or not idx.is_contiguous() or \
-                tuple(idx.shape) != (layer.B, layer.H, layer.Tq, layer.Ktot):
-            raise ValueError("idx must be contiguous int32 [B, H, Tq, Ktot]")
+        _check_idx(layer, idx, q.device)
     arr, n = dense_ranges(list(dense))
     st = _load().veda_sparse_attn(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), arr, n,
                                   float(scale), _ptr(out), _ptr(lse), _stream(stream))
@@ -342,9 +388,7 @@ def sparse_attn_fp8qk(layer: Layer, q8, k8, v, q_scale, k_scale, idx, dense: Seq
     lse = torch.empty((layer.B, layer.H, layer.query.len), dtype=torch.float32, device=v.device) \
         if want_lse else None
     if idx is not None:
-        if idx.dtype != torch.int32 or not idx.is_contiguous() or \
-                tuple(idx.shape) != (layer.B, layer.H, layer.Tq, layer.Ktot):
-            raise ValueError("idx must be contiguous int32 [B, H, Tq, Ktot]")
+        _check_idx(layer, idx, v.device)
     arr, n = dense_ranges(list(dense))
     st = _load().veda_sparse_attn_fp8qk(ctypes.byref(layer), _ptr(q8), _ptr(k8), _ptr(v), _ptr(q_scale),
                                         _ptr(k_scale), _ptr(idx), arr, n, float(scale), _ptr(out), _ptr(lse),
@@ -367,6 +411,8 @@ def layer_attn(layer: Layer, q, k, v, wq, wk, dense: Sequence[Tuple[int, int]] =
         _check_qkv(layer, out)
     if idx is None:
         idx = torch.empty((layer.B, layer.H, layer.Tq, layer.Ktot), dtype=torch.int32, device=dev)
+    else:
+        _check_idx(layer, idx, dev)
     nbytes = select_workspace_bytes(layer)
     if nbytes == 0:
         _check(_load().veda_layer_check(ctypes.byref(layer), 1), "veda_layer_attn")
@@ -400,11 +446,9 @@ def block_mass(layer: Layer, q, k, dense: Sequence[Tuple[int, int]] = (), scale:
 def block_recall(layer: Layer, mass, idx, stream=None):
     """Recall fp32 [B, H, Tq] of the index set idx [B, H, Tq, Ktot] under the teacher mass."""
     if mass.dtype != torch.float32 or tuple(mass.shape) != (layer.B, layer.H, layer.Tq, layer.Tk) \
-            or not mass.is_contiguous():
-        raise ValueError("mass must be contiguous fp32 [B, H, Tq, Tk]")
-    if idx.dtype != torch.int32 or not idx.is_contiguous() or \
-            tuple(idx.shape) != (layer.B, layer.H, layer.Tq, layer.Ktot):
-        raise ValueError("idx must be contiguous int32 [B, H, Tq, Ktot]")
+            or not mass.is_contiguous() or not mass.is_cuda:
+        raise ValueError("mass must be a contiguous fp32 [B, H, Tq, Tk] device tensor")
+    _check_idx(layer, idx, mass.device)
     rec = torch.empty((layer.B, layer.H, layer.Tq), dtype=torch.float32, device=mass.device)
     st = _load().veda_block_recall(ctypes.byref(layer), _ptr(mass), _ptr(idx), _ptr(rec), _stream(stream))
     _check(st, "veda_block_recall")

@@ -1023,9 +1023,13 @@ __device__ __forceinline__ void pingpong_attn(
   else
     body(std::integral_constant<int, 1>{});
 
-  // ---- merge group 1's partial result into group 0's (K/V stages are free now)
+  // ---- merge group 1's partial result into group 0's (K/V stages are free now).  Each
+  // wave of group 1 parks its D/32 accumulator tiles (16 floats per lane each) in sg0:
+  // (D/32) * 4 float4 per lane, so NW waves fill exactly sg0 at either head dimension.
+  constexpr int kMergeF4 = (D / 32) * 4 * 64;     // float4 slots per wave
+  static_assert(NW * kMergeF4 * sizeof(float4) <= sizeof(sg0), "merge area exceeds sg0");
   __syncthreads();
-  float4* const mo = reinterpret_cast<float4*>(sg0) + wave * 16 * 64 + lane;
+  float4* const mo = reinterpret_cast<float4*>(sg0) + wave * kMergeF4 + lane;
   if (grp) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
