@@ -154,6 +154,29 @@ int veda_select(const veda_layer* layer, const void* q, const void* k,
                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * veda_select for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * results, with the workspace taken from a library-owned device array of
+ * VEDA_NOALLOC_SCRATCH_BYTES per GPU instead of a caller buffer.  The caller still
+ * passes the inputs and outputs (q, k, wq, wk, idx, scores_opt as for veda_select).
+ *   - Allocates nothing: no hipMalloc/hipFree, no allocating library call.  The array
+ *     is held by every GPU the library runs on until the process ends.
+ *   - The array of the device current on the calling thread is used; `stream` must
+ *     belong to that device.  Its device address is looked up once per device (the
+ *     first call on a device makes that lookup, a HIP runtime call).
+ *   - Layers whose veda_select_workspace_bytes() exceeds VEDA_NOALLOC_SCRATCH_BYTES
+ *     return VEDA_EWORKSPACE before any device call (64 MiB covers q_hat + k_hat of
+ *     H = 40, p = 64 with 2741 query and 2741 key tiles).
+ *   - Calls that overlap in time on one GPU (concurrent streams or threads) share the
+ *     array and race; serialise them.  No contents need clearing between calls: every
+ *     workspace entry a call reads is written earlier in the same call.
+ */
+#define VEDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int veda_select_noalloc(const veda_layer* layer, const void* q, const void* k,
+                        const void* wq, const void* wk, int32_t* idx, float* scores_opt,
+                        void* stream);
+
+/*
  * Block-sparse attention (step a5).  For every (b, h) and query tile i, the key
  * set A(b,h,i) is the union of the tokens of the tiles idx[b,h,i,:] selects
  * (segment-local ids, segment blocks in call order, as veda_score_topk writes
