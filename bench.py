@@ -38,7 +38,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="t2v5s")
     ap.add_argument("--also", default="mid", help="second workload reported beside (or 'none')")
-    ap.add_argument("--dense-reps", type=int, default=2)
+    ap.add_argument("--dense-reps", type=int, default=0,
+                    help="reps of the dense baselines (0: 10, or 5 for layers above 200k tokens)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -270,34 +271,49 @@ def copy_calibration():
     del src, dst
 
 
+FLUSH_BYTES = 512 << 20   # written before every cold step: more than the Infinity Cache and every L2
+
+
+def timed_steps(lay, steps, flush=None):
+    """K steps, each bracketed by events on the launch stream: e0 | select | e1 | attention | e2.
+    With `flush`, a 512 MiB device write runs before every step, outside the events, so each
+    step starts with cold caches.  Returns (step_ms, select_ms, attn_ms, wall_s) lists."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(1.0)
+        ev[i][0].record()
+        lay.select()
+        ev[i][1].record()
+        lay.attn()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sel = [a.elapsed_time(b) for a, b, _ in ev]
+    att = [b.elapsed_time(c) for _, b, c in ev]
+    return [x + y for x, y in zip(sel, att)], sel, att, wall
+
+
 def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
+    """One workload.  The headline figures are cold: every step starts after a 512 MiB write
+    that evicts the Infinity Cache and the L2s, as a layer of a model does after the layers
+    before it; the same K steps run back to back (warm) are reported beside them."""
     import torch
     lay = Layer(name)
     wl = lay.wl
     for _ in range(warmup):
         lay.step()
     torch.cuda.synchronize()
-    log(f"[{name}] timing {steps} steps")
-    # events on the stream the kernels are launched on (torch's current stream, which
-    # the binding passes to the library): e0 | select | e1 | attention | e2 per step
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    s.record()
-    for i in range(steps):
-        ev[i][0].record()
-        lay.select()
-        ev[i][1].record()
-        lay.attn()
-        ev[i][2].record()
-    e.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = s.elapsed_time(e) / steps
-    sel_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    att_ms = [b.elapsed_time(c) for _, b, c in ev]
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=lay.qd.device)
+    log(f"[{name}] timing {steps} cold steps")
+    step_ms, sel_ms, att_ms, wall = timed_steps(lay, steps, flush)
+    del flush
+    log(f"[{name}] timing {steps} warm steps")
+    w_step, w_sel, w_att, w_wall = timed_steps(lay, steps)
+    ms_step = float(np.mean(step_ms))
     sel_mean, sel_min = float(np.mean(sel_ms)), float(np.min(sel_ms))
     att_mean, att_min = float(np.mean(att_ms)), float(np.min(att_ms))
     idx_np = lay.idx.cpu().numpy()
@@ -311,6 +327,14 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
         "actual_tflops_attn": flops_actual / (att_mean * 1e-3) / 1e12,
         "actual_attn_tflop": flops_actual / 1e12, "dense_equiv_tflop": flops_dense / 1e12,
         "sparsity_actual": 1.0 - flops_actual / flops_dense,
+        "selector_ms_median": float(np.median(sel_ms)), "attn_ms_median": float(np.median(att_ms)),
+        "ms_per_step_median": float(np.median(step_ms)),
+        "warm": {"ms_per_step": float(np.mean(w_step)), "ms_per_step_median": float(np.median(w_step)),
+                 "selector_ms": float(np.mean(w_sel)), "attn_ms": float(np.mean(w_att)),
+                 "attn_ms_median": float(np.median(w_att)), "attn_ms_min": float(np.min(w_att)),
+                 "actual_tflops_attn": flops_actual / (float(np.mean(w_att)) * 1e-3) / 1e12,
+                 "dense_equiv_tflops_step": flops_dense / (float(np.mean(w_step)) * 1e-3) / 1e12,
+                 "wall_s": w_wall},
     }
     # one full layer as the model runs it: also the dense (non-video) query rows
     lay.full_layer()
@@ -322,42 +346,25 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
     # pooling bandwidth: Q rows of the query segment + K rows of every key segment, once
     pool_bytes = 2.0 * wl.B * wl.H * wl.d * (wl.query.length + sum(sg.length for sg in wl.segments))
     res["pool_bytes"] = pool_bytes
-    pool_mean, pool_min, pool_med = time_events(
-        lambda: lay.B.project(lay.L, lay.qd, lay.kd, lay.wq, lay.wk), kernel_reps)
-    res["pool_ms"] = pool_mean
+    # the pooling pass alone (pool + project kernel), median of kernel_reps for both figures
+    _, _, pool_med = time_events(lambda: lay.B.project(lay.L, lay.qd, lay.kd, lay.wq, lay.wk), kernel_reps)
+    res["pool_ms"] = pool_med
     res["pool_gbs"] = pool_bytes / (pool_med * 1e-3) / 1e9
-    res["selector_ms_median"] = float(np.median(sel_ms))
-    res["attn_ms_median"] = float(np.median(att_ms))
     res["index_stats"] = index_stats(wl, idx_np)
-    # cold caches: a 512 MiB write before every step flushes the Infinity Cache and L2
-    flush = torch.empty(1 << 27, dtype=torch.float32, device=lay.qd.device)
-    cold_sel, cold_att = [], []
-    for _ in range(max(3, min(steps, 5))):
-        flush.fill_(1.0)
-        c = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        c[0].record()
-        lay.select()
-        c[1].record()
-        lay.attn()
-        c[2].record()
-        c[2].synchronize()
-        cold_sel.append(c[0].elapsed_time(c[1]))
-        cold_att.append(c[1].elapsed_time(c[2]))
-    res["cold"] = {"selector_ms_median": float(np.median(cold_sel)), "attn_ms_median": float(np.median(cold_att)),
-                   "selector_ms_min": float(np.min(cold_sel)), "attn_ms_min": float(np.min(cold_att))}
-    del flush
     if with_dense:
         Lf, wlf = lay.full_budget_layer()
         idx_full = torch.from_numpy(lay.I.full_indices(wl)).to(lay.qd.device)
         lay.attn(idx_full, Lf)
         torch.cuda.synchronize()
-        log(f"[{name}] dense baseline (every tile selected)")
-        d_mean, d_min, _ = time_events(lambda: lay.attn(idx_full, Lf), dense_reps)
+        reps = dense_reps if dense_reps > 0 else (5 if wl.n_tokens > 200_000 else 10)
+        log(f"[{name}] dense baseline (every tile selected), {reps} reps")
+        d_mean, d_min, _ = time_events(lambda: lay.attn(idx_full, Lf), reps)
+        res["dense_reps"] = reps
         res["dense_ms"] = d_mean
         res["dense_tflops"] = flops_dense / (d_mean * 1e-3) / 1e12
         res["speedup_vs_dense"] = d_mean / ms_step
         del idx_full
-        res["sdpa_dense"] = sdpa_dense(lay, dense_reps, log)
+        res["sdpa_dense"] = sdpa_dense(lay, reps, log)
         if "ms_median" in res["sdpa_dense"]:
             # the speedup is claimed against the faster of the two dense baselines
             res["speedup_vs_fastest_dense"] = min(d_mean, res["sdpa_dense"]["ms_median"]) / ms_step
@@ -487,9 +494,13 @@ def measure_fp8qk(lay, kernel_reps, log):
            "speedup_vs_bf16_attn": None,
            "max_abs_vs_bf16_out": round(float(diff.max()), 5), "mean_abs_vs_bf16_out": round(float(diff.mean()), 6),
            "kernel": f"sparse_attn_fp8qk_pingpong_kernel<{wl.d}>"}
-    del q8, k8, out8
-    torch.cuda.empty_cache()
-    return res
+    del out8
+
+    def attn8_with(idx):
+        """FP8 Q.K^T attention of this layer with the given index sets (for the parity leg)."""
+        return B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, idx, lay.dense)
+
+    return res, attn8_with
 
 
 def sdpa_dense(lay, reps, log):
@@ -526,43 +537,103 @@ def _cpu_model():
     return ""
 
 
-def cpu_baseline(lay, log, budget_s=20.0):
-    """The fp64 oracle on a bounded sample of the same layer (about budget_s of CPU
-    work), extrapolated to the whole layer."""
+SCORE_RTOL = 1e-4                 # row-normwise pooled-score bar; also the tie window
+ATTN_MAX_ABS, ATTN_MEAN_ABS = 1e-2, 1e-3
+
+
+def selection_parity(idx_gpu, sc_gpu, idx_ref, S_ref, seg_T, seg_K):
+    """Compare one head's GPU selection [Tq, Ktot] / scores [Tq, Tk] with the oracle's.
+    Returns (worst row-normwise score error, rows differing, rows differing outside the
+    tie window: a tile whose oracle score lies within SCORE_RTOL * max|s| of the k-th
+    score of its segment may go either way; every GPU row must also be a valid list)."""
+    scale = np.maximum(np.abs(S_ref).max(axis=-1), 1e-300)
+    err = float((np.abs(sc_gpu.astype(np.float64) - S_ref).max(axis=-1) / scale).max())
+    differ = np.nonzero(~np.all(idx_gpu == idx_ref, axis=-1))[0]
+    outside = 0
+    for r in differ:
+        col, kc, bad = 0, 0, False
+        for T, K in zip(seg_T, seg_K):
+            g, o = idx_gpu[r, kc:kc + K], idx_ref[r, kc:kc + K]
+            if not np.array_equal(g, o):
+                s = S_ref[r, col:col + T]
+                kth = np.sort(s)[::-1][K - 1]
+                amb = set(np.nonzero(np.abs(s - kth) <= SCORE_RTOL * scale[r])[0].tolist())
+                valid = np.all(np.diff(g) > 0) and g.min() >= 0 and g.max() < T
+                bad |= (not valid) or (set(g.tolist()) - amb != set(o.tolist()) - amb)
+            col += T
+            kc += K
+        outside += int(bad)
+    return err, int(differ.size), outside
+
+
+def cpu_baseline(lay, log, budget_s=20.0, attn8_with=None):
+    """The fp64 oracle on the same layer, timed on the host cores: selection of every head
+    (every row), then attention on random (head, query tile) pairs for about 2/3 of
+    budget_s, extrapolated to the whole layer.  Its results are compared with the GPU's
+    in the same run: the GPU's scores and index sets of every head, and the GPU's attention
+    fed the oracle's index sets on the sampled pairs."""
+    import torch
     from oracle import veda_oracle as O
     wl = lay.wl
     segs = [(s.start, s.length, s.budget) for s in wl.segments]
     query = (wl.query.start, wl.query.length)
     dense = [(r.start, r.length) for r in wl.dense]
+    seg_T = [wl.seg_tiles(s) for s in wl.segments]
+    seg_K = [min(s.budget, T) for s, T in zip(wl.segments, seg_T)]
     if lay.w.fp8:
         wq = (lay.w.wq, lay.w.pow2_exp)
         wk = (lay.w.wk, lay.w.pow2_exp)
     else:
         wq, wk = lay.w.wq, lay.w.wk
-    # selection: heads one at a time until a third of the budget is used
-    heads, t_sel = [], 0.0
-    idx_ref = None
-    for h in range(wl.H):
-        log(f"[cpu] oracle selection, head {h}")
-        t0 = time.perf_counter()
-        r, _, _, _ = O.select(lay.q, lay.k, wq, wk, wl.tile, query, segs, heads=[h])
-        t_sel += time.perf_counter() - t0
-        idx_ref = r if idx_ref is None else idx_ref
-        idx_ref[:, h] = r[:, h]
-        heads.append(h)
-        if t_sel > budget_s / 3:
-            break
-    # attention: (head, tile) pairs of the selected heads until the budget is used
+    Wq, Wk = O.weights_f64(wq), O.weights_f64(wk)
+    # GPU selection with scores, outside every timed region
+    idx_gpu, sc_gpu = lay.B.select(lay.L, lay.qd, lay.kd, lay.wq, lay.wk, want_scores=True)
+    idx_gpu = idx_gpu.cpu().numpy()
+    sc_gpu = sc_gpu.cpu().numpy()
+    torch.cuda.synchronize()
+    # oracle selection, every head
+    idx_ref = np.zeros_like(idx_gpu)
+    t_sel, score_err, rows_differ, rows_outside = 0.0, 0.0, 0, 0
+    log(f"[cpu] oracle selection of {wl.B * wl.H} heads")
+    for b in range(wl.B):
+        for h in range(wl.H):
+            t0 = time.perf_counter()
+            r, S, _, _ = O.select_head(lay.q, lay.k, Wq[h], Wk[h], b, h, wl.tile, query, segs)
+            t_sel += time.perf_counter() - t0
+            idx_ref[b, h] = r
+            e, dif, out_ = selection_parity(idx_gpu[b, h], sc_gpu[b, h], r, S, seg_T, seg_K)
+            score_err = max(score_err, e)
+            rows_differ += dif
+            rows_outside += out_
+    del sc_gpu
+    # GPU attention fed the oracle's index sets (and the FP8 Q.K^T path, if given, likewise)
+    idx_ref_dev = torch.from_numpy(idx_ref).to(lay.qd.device)
+    out_gpu = lay.B.sparse_attn(lay.L, lay.qd, lay.kd, lay.vd, idx_ref_dev, lay.dense)
+    out8 = attn8_with(idx_ref_dev) if attn8_with is not None else None
+    del idx_ref_dev
+    torch.cuda.synchronize()
+    # oracle attention on random (head, tile) pairs until the budget is used
     rng = np.random.default_rng(0)
     pairs, t_att = [], 0.0
-    while t_att < budget_s * 2 / 3 and len(pairs) < wl.H * wl.n_query_tiles:
-        pr = (0, int(rng.choice(heads)), int(rng.integers(0, wl.n_query_tiles)))
+    diffs, diffs8 = [], []
+    Tq = wl.n_query_tiles
+    while t_att < budget_s * 2 / 3 and len(pairs) < wl.B * wl.H * Tq:
+        pr = (int(rng.integers(0, wl.B)), int(rng.integers(0, wl.H)), int(rng.integers(0, Tq)))
         t0 = time.perf_counter()
-        O.attend(lay.q, lay.k, lay.v, idx_ref, wl.tile, query, segs, dense, pairs=[pr])
+        res = O.attend(lay.q, lay.k, lay.v, idx_ref, wl.tile, query, segs, dense, pairs=[pr])
         t_att += time.perf_counter() - t0
         pairs.append(pr)
+        ref = res[pr][0]
+        r0 = wl.query.start + pr[2] * wl.tile
+        got = out_gpu[pr[0], r0:r0 + ref.shape[0], pr[1]].to(torch.float64).cpu().numpy()
+        diffs.append(np.abs(got - ref).ravel())
+        if out8 is not None:
+            got8 = out8[pr[0], r0:r0 + ref.shape[0], pr[1]].to(torch.float64).cpu().numpy()
+            diffs8.append(np.abs(got8 - ref).ravel())
+    del out_gpu, out8
+    d = np.concatenate(diffs)
     log(f"[cpu] oracle attention on {len(pairs)} (head, tile) pairs")
-    layer_s = t_sel * wl.H / len(heads) + t_att * (wl.B * wl.H * wl.n_query_tiles) / len(pairs)
+    layer_s = t_sel + t_att * (wl.B * wl.H * Tq) / len(pairs)
     threads = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
@@ -571,15 +642,33 @@ def cpu_baseline(lay, log, budget_s=20.0):
             threads = min(threads, max(blas))
     except Exception:  # pragma: no cover
         pass
+    parity = {
+        "score_err": score_err, "score_bar": SCORE_RTOL,
+        "idx_rows": int(wl.B * wl.H * Tq), "idx_rows_differing": rows_differ,
+        "idx_mismatch_outside_window": rows_outside,
+        "attn_max_abs": float(d.max()), "attn_mean_abs": float(d.mean()),
+        "attn_bars": [ATTN_MAX_ABS, ATTN_MEAN_ABS], "attn_pairs": len(pairs), "attn_rows": int(d.size // wl.d),
+        "ok": bool(score_err <= SCORE_RTOL and rows_outside == 0 and d.max() <= ATTN_MAX_ABS
+                   and d.mean() <= ATTN_MEAN_ABS),
+        "what": ("GPU selection of every head and row against the oracle's (scores, index sets); GPU attention "
+                 "fed the oracle's index sets against the oracle on the sampled (head, query tile) pairs"),
+    }
+    if diffs8:
+        d8 = np.concatenate(diffs8)
+        parity["fp8qk_vs_oracle"] = {
+            "max_abs": float(d8.max()), "mean_abs": float(d8.mean()), "pairs": len(pairs),
+            "what": ("FP8 Q.K^T attention (Q, K quantised to E4M3FN) against the fp64 oracle of the bf16 "
+                     "inputs on the same pairs: the error of FP8 logits, outside the bf16 attention bar")}
+    log(f"[cpu] parity: {parity}")
     return {
         "value": lay.dense_flops() / layer_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
         "cores": threads, "kind": "oracle",
-        "sample": (f"selection on {len(heads)} of {wl.H} heads (all {wl.n_query_tiles} query tiles) in "
-                   f"{t_sel:.1f} s; attention on {len(pairs)} random (head, query tile) pairs in {t_att:.1f} s; "
-                   f"extrapolated to the whole layer: {layer_s:.0f} s per layer"),
+        "sample": (f"selection on all {wl.B * wl.H} heads (all {Tq} query tiles) in {t_sel:.1f} s; attention on "
+                   f"{len(pairs)} random (head, query tile) pairs in {t_att:.1f} s; extrapolated to the whole "
+                   f"layer: {layer_s:.0f} s per layer"),
         "layer_s_extrapolated": layer_s,
         "cpu": _cpu_model() or platform.processor() or platform.machine(),
-    }
+    }, parity
 
 
 def attention_kernel_name(wl):
@@ -636,9 +725,9 @@ def main():
     patterns = None if args.no_patterns else measure_patterns(lay, args.kernel_reps, log)
     if patterns is not None:
         patterns["random_indices"] = random_pattern(lay, args.kernel_reps, log)
-    fp8qk = None
+    fp8qk, attn8_with = None, None
     if not args.no_fp8 and lay.wl.tile == 128:
-        fp8qk = measure_fp8qk(lay, args.kernel_reps, log)
+        fp8qk, attn8_with = measure_fp8qk(lay, args.kernel_reps, log)
         fp8qk["speedup_vs_bf16_attn"] = round(res["attn_ms_median"] / fp8qk["attn_ms_median"], 3)
     peaks = device_peaks(log)
     also = None
@@ -662,9 +751,13 @@ def main():
                                                        "sparsity_actual")}
             import torch
             torch.cuda.empty_cache()
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lay, log)
+        cpu, parity = cpu_baseline(lay, log, attn8_with=attn8_with)
+        if fp8qk is not None and "fp8qk_vs_oracle" in parity:
+            fp8qk["vs_oracle_bf16_inputs"] = parity.pop("fp8qk_vs_oracle")
+    attn8_with = None
+    torch.cuda.empty_cache()
     achieved = res["actual_tflops_attn"]
     traffic = recorded_traffic(args.workload)
     attn_kernel = attention_kernel_name(wl)
@@ -696,7 +789,11 @@ def main():
         "mfma_util_vs_measured_peak": round(achieved / peaks["mfma_bf16_tflops"], 4),
         "selector_ms_median": round(res["selector_ms_median"], 4),
         "attn_ms_median": round(res["attn_ms_median"], 4),
-        "cold": {k: round(v, 4) for k, v in res["cold"].items()},
+        "ms_per_step_median": round(res["ms_per_step_median"], 4),
+        "warm": {k: round(v, 4) for k, v in res["warm"].items()},
+        "protocol": {"headline": "cold: a 512 MiB device write before every step, outside the step's events",
+                     "warm": "the same steps back to back", "statistic": "mean over the timed steps",
+                     "dense_reps": res.get("dense_reps")},
         "pool": {"ms": round(res["pool_ms"], 4), "gbs": round(res["pool_gbs"], 1),
                  "frac_hbm_peak": round(res["pool_gbs"] / PEAK_HBM_GBS, 4),
                  "frac_copy": round(res["pool_gbs"] / peaks["copy_gbs"], 4),
@@ -713,6 +810,7 @@ def main():
                      "traffic_unit": "GB per launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel": attn_kernel, "algorithmic": f"{res['actual_attn_tflop']:.3f} TFLOP per launch"},
         "cpu_baseline": cpu,
+        "parity": parity,
         "patterns": patterns,
         "fp8qk": fp8qk,
         "also": also,

@@ -217,22 +217,32 @@ def select(q_bits, k_bits, wq, wk, tile: int, query: Tuple[int, int],
     KH = np.zeros((B, H, Tk, p), dtype=np.float64)
     for b in range(B):
         for h in heads:
-            q_hat = project(pool_tiles(q_bits, b, h, query[0], query[1], tile), Wq[h])
-            k_hat = np.concatenate(
-                [project(pool_tiles(k_bits, b, h, st, ln, tile), Wk[h]) for (st, ln, _) in segments],
-                axis=0)
-            s = tile_scores(q_hat, k_hat)
-            QH[b, h] = q_hat
-            KH[b, h] = k_hat
-            S[b, h] = s
-            col = 0
-            kc = 0
-            for (st, ln, bud), T, K in zip(segments, Ts, Ks):
-                for i in range(Tq):
-                    idx[b, h, i, kc:kc + K] = topk_lowest_index(s[i, col:col + T], bud)
-                col += T
-                kc += K
+            idx[b, h], S[b, h], QH[b, h], KH[b, h] = select_head(q_bits, k_bits, Wq[h], Wk[h], b, h, tile,
+                                                                query, segments)
     return idx, S, QH, KH
+
+
+def select_head(q_bits, k_bits, wq_h: np.ndarray, wk_h: np.ndarray, b: int, h: int, tile: int,
+                query: Tuple[int, int], segments: Sequence[Tuple[int, int, int]]):
+    """O3..O6 for one (batch, head); wq_h / wk_h are that head's float64 [p, d] weights.
+    Returns (idx int32 [Tq, Ktot], scores float64 [Tq, sum T_s], q_hat [Tq, p],
+    k_hat [sum T_s, p])."""
+    Tq = -(-query[1] // tile)
+    Ts = [-(-ln // tile) for (_, ln, _) in segments]
+    Ks = [min(bud, T) for (_, _, bud), T in zip(segments, Ts)]
+    q_hat = project(pool_tiles(q_bits, b, h, query[0], query[1], tile), wq_h)
+    k_hat = np.concatenate(
+        [project(pool_tiles(k_bits, b, h, st, ln, tile), wk_h) for (st, ln, _) in segments], axis=0)
+    s = tile_scores(q_hat, k_hat)
+    idx = np.zeros((Tq, sum(Ks)), dtype=np.int32)
+    col = 0
+    kc = 0
+    for (st, ln, bud), T, K in zip(segments, Ts, Ks):
+        for i in range(Tq):
+            idx[i, kc:kc + K] = topk_lowest_index(s[i, col:col + T], bud)
+        col += T
+        kc += K
+    return idx, s, q_hat, k_hat
 
 
 # ----------------------------------------------------------------------------- O7

@@ -61,3 +61,29 @@ def test_seed_replaces_every_workloads_input_seed():
     assert (w7.n_tokens, w7.segments, w7.dense) == (base.n_tokens, base.segments, base.dense)
     q0, q7 = I.make_qkv(base)[0], I.make_qkv(w7)[0]
     assert q0.shape == q7.shape and not np.array_equal(q0, q7)
+
+
+def test_selection_parity_counts_only_mismatches_outside_the_tie_window():
+    import numpy as np
+    bench = _bench()
+    # one segment of 6 tiles, k = 2; row 0: tiles 1 and 4 tie exactly for the 2nd place
+    S = np.array([[0.0, 5.0, 1.0, 2.0, 5.0, 9.0],
+                  [9.0, 8.0, 1.0, 0.5, 0.25, 0.0]])
+    ref = np.array([[1, 5], [0, 1]], dtype=np.int32)
+    sc = S.astype(np.float32)
+    # identical
+    assert bench.selection_parity(ref.copy(), sc, ref, S, [6], [2]) == (0.0, 0, 0)
+    # the tie goes the other way: differs, but inside the window
+    g = np.array([[4, 5], [0, 1]], dtype=np.int32)
+    err, differ, outside = bench.selection_parity(g, sc, ref, S, [6], [2])
+    assert (differ, outside) == (1, 0)
+    # a clear mismatch in row 1
+    g = np.array([[1, 5], [0, 2]], dtype=np.int32)
+    assert bench.selection_parity(g, sc, ref, S, [6], [2])[1:] == (1, 1)
+    # an invalid (not ascending) row counts as outside
+    g = np.array([[5, 4], [0, 1]], dtype=np.int32)
+    assert bench.selection_parity(g, sc, ref, S, [6], [2])[1:] == (1, 1)
+    # score error is row-normwise
+    sc2 = sc.copy()
+    sc2[1, 3] += 9.0 * 2e-4
+    assert abs(bench.selection_parity(ref, sc2, ref, S, [6], [2])[0] - 2e-4) < 1e-6

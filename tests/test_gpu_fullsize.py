@@ -1,8 +1,18 @@
-"""GPU parity at the full layer sizes, in the launch configuration the benchmark
-times: the GPU runs the whole layer; the oracle checks every row of sampled
-heads for selection, and sampled (head, query tile) pairs for attention (first
-tile, last tile, a tile that straddles a frame boundary, and random ones)."""
+"""GPU parity at the full layer sizes, in the launch configuration the benchmark times.
+
+* Selection: the GPU selects the whole layer; the oracle selects every head as well,
+  and scores and index sets are compared on every row of every head.
+* Attention fed the oracle's indices: sampled (head, query tile) pairs (first tile,
+  last tile, a tile that straddles a frame boundary, random ones) on several heads.
+* The full-layer call (video rows sparse, every other query row dense over all keys):
+  the call's own index sets equal the selection's; sampled video tiles and sampled
+  windows of every dense query range (first and last rows, range boundaries) are
+  compared with the oracle.  At the 14.4 s layer the dense query rows list 5522 key
+  blocks, more than the two-group kernel's table, so this reaches the single-pipeline
+  kernel at that length.
+"""
 import gc
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -12,14 +22,66 @@ from block_sparse_attention_predictor_amd import binding as Bnd
 from block_sparse_attention_predictor_amd import inputs as I
 from oracle import veda_oracle as O
 
-from gpu_util import bf16_to_f64, check_attn, check_indices, check_scores, to_dev, to_dev_bf16
+from gpu_util import check_attn, check_indices, check_scores, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
+ORACLE_THREADS = 16
 
-@pytest.fixture(autouse=True)
-def _free():
-    yield
+
+class Inputs:
+    def __init__(self, name):
+        wl = I.WORKLOADS[name]
+        print(f"[{name}] generating inputs", flush=True)
+        self.wl = wl
+        self.q, self.k, self.v = I.make_qkv(wl)
+        w = I.make_weights(wl)
+        if w.fp8:
+            # the path as it runs: FP8 weights dequantised on the GPU at load
+            self.wq = Bnd.dequant_fp8_e4m3(to_dev(w.wq), w.pow2_exp)
+            self.wk = Bnd.dequant_fp8_e4m3(to_dev(w.wk), w.pow2_exp)
+            self.wq_ref, self.wk_ref = (w.wq, w.pow2_exp), (w.wk, w.pow2_exp)
+            for dev_w, codes in ((self.wq, w.wq), (self.wk, w.wk)):
+                bits = O.dequant_e4m3fn_to_bf16_bits(codes, w.pow2_exp)
+                assert np.array_equal(dev_w.view(torch.int16).cpu().numpy().view(np.uint16), bits)
+        else:
+            self.wq, self.wk = to_dev_bf16(w.wq), to_dev_bf16(w.wk)
+            self.wq_ref, self.wk_ref = w.wq, w.wk
+        self.qd, self.kd, self.vd = to_dev_bf16(self.q), to_dev_bf16(self.k), to_dev_bf16(self.v)
+        self.L = Bnd.layer_from_workload(wl)
+        self.segs = [(s.start, s.length, s.budget) for s in wl.segments]
+        self.dense = [(r.start, r.length) for r in wl.dense]
+        self.query = (wl.query.start, wl.query.length)
+        self.seg_T = [wl.seg_tiles(s) for s in wl.segments]
+        self.seg_K = [min(s.budget, T) for s, T in zip(wl.segments, self.seg_T)]
+        self._sel = None
+
+    def oracle_selection(self):
+        """Oracle indices and scores of every head, [B, H, Tq, Ktot] and [B, H, Tq, Tk]."""
+        if self._sel is None:
+            wl = self.wl
+            Wq, Wk = O.weights_f64(self.wq_ref), O.weights_f64(self.wk_ref)
+            jobs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+            print(f"[{wl.name}] oracle selection of {len(jobs)} heads", flush=True)
+
+            def one(bh):
+                b, h = bh
+                idx, s, _, _ = O.select_head(self.q, self.k, Wq[h], Wk[h], b, h, wl.tile, self.query, self.segs)
+                return idx, s
+
+            with ThreadPoolExecutor(ORACLE_THREADS) as ex:
+                res = list(ex.map(one, jobs))
+            idx = np.stack([r[0] for r in res]).reshape(wl.B, wl.H, *res[0][0].shape)
+            S = np.stack([r[1] for r in res]).reshape(wl.B, wl.H, *res[0][1].shape)
+            self._sel = (idx, S)
+        return self._sel
+
+
+@pytest.fixture(scope="module", params=["t2v5s", "r2va", "t2v14s"])
+def layer(request):
+    x = Inputs(request.param)
+    yield x
+    del x
     gc.collect()
     torch.cuda.empty_cache()
 
@@ -33,57 +95,102 @@ def sampled_tiles(wl, rng, extra=2):
     return sorted(tiles)
 
 
-@pytest.mark.parametrize("name", ["t2v5s", "r2va", "t2v14s"])
-def test_full_layer_parity(name):
-    wl = I.WORKLOADS[name]
-    print(f"[{name}] generating inputs", flush=True)
-    q, k, v = I.make_qkv(wl)
-    w = I.make_weights(wl)
-    rng = np.random.default_rng(wl.index)
-    if w.fp8:
-        # the path as it runs: FP8 weights dequantised on the GPU at load
-        wq = Bnd.dequant_fp8_e4m3(to_dev(w.wq), w.pow2_exp)
-        wk = Bnd.dequant_fp8_e4m3(to_dev(w.wk), w.pow2_exp)
-        wq_bits = O.dequant_e4m3fn_to_bf16_bits(w.wq, w.pow2_exp)
-        wk_bits = O.dequant_e4m3fn_to_bf16_bits(w.wk, w.pow2_exp)
-        assert np.array_equal(wq.view(torch.int16).cpu().numpy().view(np.uint16), wq_bits)
-        assert np.array_equal(wk.view(torch.int16).cpu().numpy().view(np.uint16), wk_bits)
-    else:
-        wq_bits, wk_bits = w.wq, w.wk
-        wq, wk = to_dev_bf16(w.wq), to_dev_bf16(w.wk)
-    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
-    L = Bnd.layer_from_workload(wl)
-    segs = [(s.start, s.length, s.budget) for s in wl.segments]
-    dense = [(r.start, r.length) for r in wl.dense]
-    print(f"[{name}] GPU select", flush=True)
-    idx, sc = Bnd.select(L, qd, kd, wq, wk, want_scores=True)
-    torch.cuda.synchronize()
-    heads = [0, wl.H // 2, wl.H - 1]
-    print(f"[{name}] oracle select on heads {heads}", flush=True)
-    idx_ref, S_ref, _, _ = O.select(q, k, wq_bits, wk_bits, wl.tile, (wl.query.start, wl.query.length),
-                                    segs, heads=heads)
-    idx_np = idx.cpu().numpy()
-    sc_np = sc[:, heads].cpu().numpy().astype(np.float64)
-    del sc
-    seg_T = [wl.seg_tiles(s) for s in wl.segments]
-    seg_K = [min(s.budget, T) for s, T in zip(wl.segments, seg_T)]
-    check_scores(sc_np, S_ref[:, heads])
-    ties = check_indices(idx_np[:, heads], idx_ref[:, heads], S_ref[:, heads], seg_T, seg_K)
-    print(f"[{name}] selection ok ({ties} rows decided inside the tie window)", flush=True)
+def sampled_heads(wl, rng, extra=2):
+    heads = {0, wl.H // 2, wl.H - 1}
+    heads |= set(rng.integers(1, wl.H - 1, extra).tolist())
+    return sorted(heads)
 
-    # attention with the oracle's indices on the sampled heads
-    idx_np[:, heads] = idx_ref[:, heads]
-    out = Bnd.sparse_attn(L, qd, kd, vd, to_dev(idx_np), dense)
-    torch.cuda.synchronize()
-    tiles = sampled_tiles(wl, rng)
-    pairs = [(0, h, t) for h in heads for t in tiles]
-    print(f"[{name}] oracle attention on {len(pairs)} (head, tile) pairs", flush=True)
-    res = O.attend(q, k, v, idx_np, wl.tile, (wl.query.start, wl.query.length), segs, dense,
-                   pairs=pairs)
+
+def compare_tiles(x, out, idx_np, pairs):
+    """Oracle attention of the (b, h, query tile) pairs with the given index sets against
+    the GPU output rows."""
+    wl = x.wl
+    res = O.attend(x.q, x.k, x.v, idx_np, wl.tile, x.query, x.segs, x.dense, pairs=pairs)
     got = []
     for (b, h, t) in res:
         r0 = wl.query.start + t * wl.tile
         r1 = wl.query.start + min((t + 1) * wl.tile, wl.query.length)
         got.append(out[b, r0:r1, h].to(torch.float64).cpu().numpy())
-    mx, mean = check_attn(np.concatenate(got), np.concatenate([r[0] for r in res.values()]))
-    print(f"[{name}] attention ok: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+    return check_attn(np.concatenate(got), np.concatenate([r[0] for r in res.values()]))
+
+
+def test_selection_every_head(layer):
+    x, wl = layer, layer.wl
+    print(f"[{wl.name}] GPU select", flush=True)
+    idx, sc = Bnd.select(x.L, x.qd, x.kd, x.wq, x.wk, want_scores=True)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    sc_np = sc.cpu().numpy()
+    del sc
+    idx_ref, S_ref = x.oracle_selection()
+    worst, ties = 0.0, 0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            worst = max(worst, check_scores(sc_np[b, h].astype(np.float64), S_ref[b, h]))
+            ties += check_indices(idx_np[b, h], idx_ref[b, h], S_ref[b, h], x.seg_T, x.seg_K)
+    print(f"[{wl.name}] selection ok on {wl.B * wl.H} heads x {wl.n_query_tiles} rows: "
+          f"score error {worst:.2e}, {ties} rows decided inside the tie window", flush=True)
+
+    # attention with the oracle's indices (every head's), sampled pairs
+    rng = np.random.default_rng(wl.index)
+    out = Bnd.sparse_attn(x.L, x.qd, x.kd, x.vd, to_dev(idx_ref), x.dense)
+    torch.cuda.synchronize()
+    pairs = [(0, h, t) for h in sampled_heads(wl, rng) for t in sampled_tiles(wl, rng)]
+    print(f"[{wl.name}] oracle attention on {len(pairs)} (head, tile) pairs", flush=True)
+    mx, mean = compare_tiles(x, out, idx_ref, pairs)
+    print(f"[{wl.name}] attention ok: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+
+
+def dense_query_ranges(wl):
+    """Every non-video query range of the layer: reference image, text, VLM, audio."""
+    return ([(s.start, s.length) for s in wl.segments if s.name != "video"] +
+            [(r.start, r.length) for r in wl.dense])
+
+
+def dense_row_windows(ranges, tile, rows=64):
+    """Row windows to compare: the first and last rows of every range, rows around every
+    boundary between two touching ranges, and the last tile of the merged launch."""
+    wins = []
+    for st, ln in ranges:
+        wins.append((st, min(rows, ln)))
+        wins.append((st + ln - min(rows, ln), min(rows, ln)))
+    starts = {st for st, _ in ranges}
+    for st, ln in ranges:
+        if st + ln in starts:
+            wins.append((st + ln - rows // 2, rows))
+    lo = min(st for st, _ in ranges)
+    hi = max(st + ln for st, ln in ranges)
+    last = lo + ((hi - lo - 1) // tile) * tile
+    wins.append((last, hi - last))
+    return sorted(set(wins))
+
+
+def test_full_layer_call(layer):
+    x, wl = layer, layer.wl
+    dq = dense_query_ranges(wl)
+    print(f"[{wl.name}] GPU full layer: {len(dq)} dense query ranges, {sum(n for _, n in dq)} rows", flush=True)
+    out, idx = Bnd.layer_attn(x.L, x.qd, x.kd, x.vd, x.wq, x.wk, x.dense, dq)
+    torch.cuda.synchronize()
+    # the layer call selects exactly as veda_select does
+    idx_sel = Bnd.select(x.L, x.qd, x.kd, x.wq, x.wk)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_sel)
+    idx_np = idx.cpu().numpy()
+    rng = np.random.default_rng(wl.index + 7)
+    heads = sampled_heads(wl, rng, extra=0)
+    # video rows: sparse attention over the index sets the call chose
+    pairs = [(0, h, t) for h in heads for t in sampled_tiles(wl, rng, extra=1)]
+    mx, mean = compare_tiles(x, out, idx_np, pairs)
+    print(f"[{wl.name}] video rows ok: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+    # every other query row attends to every key
+    wins = dense_row_windows(dq, wl.tile)
+    got, ref = [], []
+
+    jobs = [(h, w) for h in heads for w in wins]
+    print(f"[{wl.name}] oracle dense attention on {len(jobs)} (head, row window) pairs", flush=True)
+    for h, (st, ln) in jobs:
+        r, _ = O.attend_all_keys(x.q, x.k, x.v, 0, h, (st, ln), x.segs, x.dense)
+        got.append(out[0, st:st + ln, h].to(torch.float64).cpu().numpy())
+        ref.append(r)
+    mx, mean = check_attn(np.concatenate(got), np.concatenate(ref))
+    print(f"[{wl.name}] dense query rows ok: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
