@@ -217,11 +217,11 @@ def index_stats(wl, idx_np):
 def device_peaks(log):
     """What this device reaches on an MFMA-only loop and on a plain 1 GiB copy."""
     import torch
-    B = __import__("block_sparse_attention_predictor_amd.binding", fromlist=["x"])
-    B.mfma_peak(50, 2048)
+    from block_sparse_attention_predictor_amd import probe
+    probe.mfma_peak(50, 2048)
     torch.cuda.synchronize()
-    ms, _, _ = time_events(lambda: B.mfma_peak(2000, 2048), 3)
-    _, flops = B.mfma_peak(1, 1)
+    ms, _, _ = time_events(lambda: probe.mfma_peak(2000, 2048), 3)
+    _, flops = probe.mfma_peak(1, 1)
     flops *= 2000 * 2048
     n = 1 << 29
     src = torch.ones(n, dtype=torch.bfloat16, device="cuda")

@@ -112,7 +112,6 @@ def _load():
         "veda_st_metadata_count": (ctypes.c_int64, [P]),
         "veda_st_metadata_at": (ctypes.c_int, [P, ctypes.c_int64, ctypes.POINTER(ctypes.c_char_p),
                                                ctypes.POINTER(ctypes.c_char_p)]),
-        "veda_mfma_peak": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P]),
         "veda_window_width": (ctypes.c_int64, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32]),
         "veda_window_indices": (ctypes.c_int, [L, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -134,12 +133,12 @@ def exported_symbols():
                         "veda_window_indices", "veda_block_mass", "veda_block_recall",
                         "veda_st_open", "veda_st_close", "veda_st_count", "veda_st_info",
                         "veda_st_find", "veda_st_read", "veda_st_metadata_count",
-                        "veda_st_metadata_at", "veda_mfma_peak", "veda_sparse_attn_fp8qk",
+                        "veda_st_metadata_at", "veda_sparse_attn_fp8qk",
                         "veda_quantize_fp8_e4m3")]
 
 
 # VEDA_ABI_VERSION of include/veda.h that this binding marshals for
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def abi_version() -> int:
@@ -480,13 +479,6 @@ def window_indices(layer: Layer, frame_tokens: int, chunk_frames: int = 5, halo_
     att = Layer.from_buffer_copy(layer)
     att.budget[0] = width
     return idx, att
-
-
-def mfma_peak(iters: int = 2000, workgroups: int = 2048, stream=None):
-    """Launch the MFMA-only loop; returns (checksum buffer, flops of the launch)."""
-    out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
-    _check(_load().veda_mfma_peak(_ptr(out), int(iters), int(workgroups), _stream(stream)), "veda_mfma_peak")
-    return out, 2097152.0 * iters * workgroups
 
 
 # ----------------------------------------------------------------------------- predictor files

@@ -82,9 +82,6 @@ hipError_t launch_window_indices(int64_t q0, int64_t qlen, int64_t tile, int64_t
                                  int32_t BH, const WindowPattern& P, int32_t* idx, int32_t kmax,
                                  hipStream_t s);
 
-// MFMA-only loop (measurement aid, see probe.hip).
-hipError_t launch_mfma_peak(float* out, int32_t iters, int32_t workgroups, hipStream_t s);
-
 // Rows of the score block one selection workgroup handles for Tk key tiles.
 int score_rows_per_block(int Tk);
 

@@ -1,9 +1,11 @@
-// Measurement aid: the bf16 matrix-core rate an MFMA-only loop reaches on this
-// device, the reference against which the attention kernel's MFMA use is also
-// reported (besides the 2.5 PFLOP/s specification).
-#include "common.h"
+// Measurement aid (libveda_probe.so, declared in include/veda_probe.h): the bf16
+// matrix-core rate an MFMA-only loop reaches on this device, the reference against
+// which a benchmark also reports the attention kernel's MFMA use (besides the
+// 2.5 PFLOP/s specification).  Not part of the method's library.
+#include "../../include/veda_probe.h"
 
-namespace veda {
+#include <hip/hip_runtime.h>
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -37,9 +39,9 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* __restrict__ out,
 
 }  // namespace
 
-hipError_t launch_mfma_peak(float* out, int32_t iters, int32_t workgroups, hipStream_t s) {
-  hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)workgroups), dim3(256), 0, s, out, iters);
-  return hipGetLastError();
+extern "C" int veda_probe_mfma_peak(float* out, int32_t iters, int32_t workgroups, void* stream) {
+  if (!out || iters < 1 || workgroups < 1) return -1;
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream, out,
+                     iters);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
 }
-
-}  // namespace veda

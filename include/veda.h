@@ -14,7 +14,9 @@
  * Conventions shared by every entry point
  *   - Every buffer is caller-owned device memory (hipMalloc'd or torch-allocated).
  *     The library never allocates or frees device memory, keeps no pointer after
- *     a call returns and has no mutable global state: calls are re-entrant.
+ *     a call returns and has no mutable global state: calls are re-entrant.  The one
+ *     exception is veda_select_noalloc, whose workspace is a library-owned device array
+ *     per GPU (see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *     work is enqueued asynchronously on it; nothing is synchronised.  A device
  *     fault surfaces at the caller's next synchronisation.
@@ -39,7 +41,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 3
+#define VEDA_ABI_VERSION 4
 #define VEDA_MAX_SEGMENTS 4
 #define VEDA_MAX_DENSE 8
 #define VEDA_MAX_KEY_TILES 8192   /* sum over segments of T_s accepted by selection */
@@ -114,7 +116,10 @@ int veda_layer_check(const veda_layer* layer, int for_select);
 size_t veda_select_workspace_bytes(const veda_layer* layer);
 
 /*
- * Pool and project (steps a1 + a2).
+ * Pool and project (steps a1 + a2).  Affine launch article, "Training the Selector,
+ * Not the Generator": the trained selector is a query projection and a key projection
+ * (one tensor each per layer, "How the SN120 Competition Works"); the pooling to one
+ * vector per token tile is this library's reading of its "lightweight predictor".
  * For every (b, h) and tile i of the query segment:
  *     q_bar[i] = mean of Q[b, n, h, :] over the real tokens n of tile i (fp32 sums),
  *     q_hat[b, h, i, :] = Wq[h] q_bar[i]      (Wq[h] is p x d, row-major, no bias);
@@ -131,7 +136,9 @@ int veda_pool_project(const veda_layer* layer, const void* q, const void* k,
                       void* stream);
 
 /*
- * Score and select (steps a3 + a4), from veda_pool_project's outputs.
+ * Score and select (steps a3 + a4), from veda_pool_project's outputs.  Veda R2VA
+ * record, first paragraph: a fixed budget of key tiles per query tile and head, the
+ * reference and current-video segments chosen independently (one budget per segment).
  *     S[b, h, i, j] = <q_hat[b,h,i,:], k_hat[b,h,j,:]>    (unscaled)
  * For every (b, h, i) and segment s, the min(budget[s], T_s) tiles of segment s
  * with the largest S; equal scores go to the lower tile index (-0 equals +0).
@@ -145,7 +152,9 @@ int veda_score_topk(const veda_layer* layer, const float* q_hat, const float* k_
                     int32_t* idx, float* scores_opt, void* stream);
 
 /*
- * Full selection: veda_pool_project into the workspace, then veda_score_topk.
+ * Full selection: veda_pool_project into the workspace, then veda_score_topk (the
+ * selector of the Affine launch article, "Training the Selector, Not the Generator",
+ * with the per-segment budgets of the Veda R2VA record, first paragraph).
  *   ws, ws_bytes : device workspace of at least veda_select_workspace_bytes(layer),
  *                  256-byte aligned.  Its contents are scratch.
  */
@@ -177,7 +186,10 @@ int veda_select_noalloc(const veda_layer* layer, const void* q, const void* k,
                         void* stream);
 
 /*
- * Block-sparse attention (step a5).  For every (b, h) and query tile i, the key
+ * Block-sparse attention (step a5).  Affine launch article, "Training the Selector,
+ * Not the Generator": the selected blocks feed a sparse execution kernel; Veda R2VA
+ * record, first paragraph: text, VLM conditioning and audio keys stay dense (the
+ * `dense` ranges).  For every (b, h) and query tile i, the key
  * set A(b,h,i) is the union of the tokens of the tiles idx[b,h,i,:] selects
  * (segment-local ids, segment blocks in call order, as veda_score_topk writes
  * them) and of every dense range.  For each query row n of tile i:
@@ -342,16 +354,6 @@ int veda_window_indices(const veda_layer* layer, int64_t frame_tokens, int32_t c
  */
 int veda_dequant_fp8_e4m3(const uint8_t* src, void* dst_bf16, int64_t n, int32_t pow2_exp,
                           void* stream);
-
-/*
- * Measurement aid (not part of the method): an MFMA-only loop, so that the attention
- * kernel's matrix-core use can be reported against the rate this device actually
- * reaches as well as against the specification.  Each of `workgroups` workgroups of
- * 256 threads runs iters x 16 products of v_mfma_f32_32x32x16_bf16 per wave
- * (32768 flops each): 2,097,152 * iters * workgroups flops in total.  out: fp32 device
- * buffer of workgroups * 256 elements (receives checksums).  Asynchronous on stream.
- */
-int veda_mfma_peak(float* out, int32_t iters, int32_t workgroups, void* stream);
 
 /*
  * safetensors reader (host only) for predictor files: the competition's selector

@@ -314,9 +314,6 @@ void fuzz_plain_calls(Rng& r) {
     const int st = veda_dequant_fp8_e4m3(static_cast<const uint8_t*>(dev(50)), dev(51, r.chance(5) ? 1 : 0),
                                          n, e, nullptr);
     check_status("veda_dequant_fp8_e4m3", st, c);
-    Call c2(dummy);
-    const int st2 = veda_mfma_peak(static_cast<float*>(dev(52)), r.pick(kI32), r.pick(kI32), nullptr);
-    check_status("veda_mfma_peak", st2, c2);
   }
   for (int s = -12; s <= 2; ++s) EXPECT(veda_status_string(s) != nullptr, "veda_status_string", s);
   EXPECT(veda_layer_check(nullptr, 0) == VEDA_EINVAL, "veda_layer_check", 0);

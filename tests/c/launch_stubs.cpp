@@ -203,11 +203,6 @@ hipError_t launch_window_indices(int64_t q0, int64_t qlen, int64_t tile, int64_t
   return done();
 }
 
-hipError_t launch_mfma_peak(float* out, int32_t iters, int32_t workgroups, hipStream_t) {
-  REQUIRE(out && iters >= 1 && workgroups >= 1);
-  return done();
-}
-
 int score_rows_per_block(int) { return 1; }
 
 }  // namespace veda

@@ -17,8 +17,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(Bnd.lib_path),
                                 reason="libveda.so not built (run __graft_entry__.build())")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(veda_[a-z0-9_]+)\s*\(", text)))
 
@@ -37,7 +37,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert Bnd.abi_version() == 3 == Bnd.ABI_VERSION
+    assert Bnd.abi_version() == 4 == Bnd.ABI_VERSION
     for code in range(-8, 1):
         assert Bnd.status_string(code) and "unknown" not in Bnd.status_string(code)
     assert "unknown" in Bnd.status_string(-99)
@@ -269,12 +269,22 @@ def test_block_mass_and_recall_checks_before_device_calls():
     assert lib.veda_block_recall(ctypes.byref(_layer(d=96)), fake, fake, fake, None) == -2
 
 
-def test_mfma_peak_argument_checks():
-    lib = Bnd._load()
+def test_probe_library_is_separate_and_exports_its_header():
+    """The MFMA-only measurement loop lives in libveda_probe.so (include/veda_probe.h), not in
+    the method's library or header."""
+    from block_sparse_attention_predictor_amd import probe
+    names = declared_functions(os.path.join(ROOT, "include", "veda_probe.h"))
+    assert names == sorted(probe.exported_symbols())
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.lib_path], capture_output=True, text=True).stdout
+    assert set(names) <= set(re.findall(r"\sT\s(veda_\w+)", out))
+    main = subprocess.run(["nm", "-D", "--defined-only", Bnd.lib_path], capture_output=True, text=True).stdout
+    assert not any("probe" in n or "mfma_peak" in n for n in re.findall(r"\sT\s(veda_\w+)", main))
+    assert not any("probe" in n or "mfma_peak" in n for n in declared_functions())
+    lib = probe._load()
     fake = ctypes.c_void_p(0x10000)
-    assert lib.veda_mfma_peak(None, 10, 4, None) == -1
-    assert lib.veda_mfma_peak(fake, 0, 4, None) == -1
-    assert lib.veda_mfma_peak(fake, 10, 0, None) == -1
+    assert lib.veda_probe_mfma_peak(None, 10, 4, None) == -1
+    assert lib.veda_probe_mfma_peak(fake, 0, 4, None) == -1
+    assert lib.veda_probe_mfma_peak(fake, 10, 0, None) == -1
 
 
 def test_package_entry_points_resolve():
