@@ -6,18 +6,21 @@
 // dot product <q_hat_i, k_hat_j> of the projected pooled vectors; ties go to
 // the lower tile index and the chosen ids are written ascending.
 //
-// One workgroup (4 waves) owns R consecutive query-tile rows of one (b, h):
+// One workgroup (16 waves for predictor widths up to 64, 8 up to 128, else 4) owns R
+// consecutive query-tile rows of one (b, h):
 //  1. S[R x Tk] on bf16 matrix cores: each fp32 operand x is split into
 //     hi = bf16(x) and lo = bf16(x - hi); S = hi*hi + hi*lo + lo*hi (the lo*lo
 //     term is below 2^-16 relative).  v_mfma_f32_16x16x32_bf16 blocks of 16 key
 //     tiles are spread over the waves; the scores land in LDS as order-preserving
 //     uint32 keys (and optionally in HBM as fp32).
 //  2. Each (row, segment) pair is reduced by one wave: a most-significant-digit
-//     radix select (four 8-bit passes, histograms in LDS, one wave-wide scan per
-//     pass) finds the k-th largest key exactly and how many keys equal to it are
-//     kept; one ordered pass with wave ballots then writes every key above the
-//     threshold and the first of the equal ones, which yields the lowest-index
-//     tie-break and an ascending list without sorting.
+//     radix select (up to four 8-bit steps, histograms in LDS, one wave-wide scan per
+//     step, stopping once the fixed bits decide the set) finds the k-th largest key
+//     exactly and how many keys equal to it are kept; one ordered pass with wave
+//     ballots then writes every key above the threshold and the first of the equal
+//     ones, which yields the lowest-index tie-break and an ascending list without
+//     sorting.  Each step is a chain of dependent LDS round trips, so the many waves
+//     of a workgroup (one row each) are what keeps the CU busy.
 #include "common.h"
 
 namespace veda {
@@ -26,9 +29,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kHistCopies = 4;                 // radix histograms per wave
+constexpr int kChunk = 16;                     // keys per lane read ahead in a radix pass
+
+// histogram words of one wave: kCopies histograms of 256 digits, plus one word per lane
+// that takes the updates of keys outside the current prefix (no branch per key)
+constexpr int hist_words(int copies) { return copies * 256 + 64; }
 
 // float -> uint32 whose unsigned order is the float order; -0 maps like +0
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -50,8 +55,22 @@ __device__ __forceinline__ int prefix_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-template <int kMaxKSteps>
-__global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS round trip):
+// Hillis-Steele steps inside each row of 16 lanes, then the last lane of row 0 (2) is
+// added to row 1 (3), and lane 31 to rows 2 and 3.  Moves from outside a row or masked
+// rows contribute 0.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return x;
+}
+
+template <int kMaxKSteps, int kWaves, int kHistCopies>
+__global__ __launch_bounds__(64 * kWaves) void score_topk_kernel(LayerDev L, int R,
                                                               const float* __restrict__ q_hat,
                                                               const float* __restrict__ k_hat,
                                                               int32_t* __restrict__ idx,
@@ -59,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
   extern __shared__ uint32_t smem[];
   const int Tk = L.Tk;
   uint32_t* keys = smem;                       // [R][Tk]
-  uint32_t* hist_all = smem + (size_t)R * Tk;  // [kWaves][kHistCopies][256]
+  uint32_t* hist_all = smem + (size_t)R * Tk;  // [kWaves][hist_words(kHistCopies)]
 
   const int b = blockIdx.z;
   const int h = blockIdx.y;
@@ -153,9 +172,11 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
   __syncthreads();
 
   // ---- 2. top-k per (row, segment), one wave each ------------------------------------
-  // each wave keeps kHistCopies histograms (lane % kHistCopies picks one) so lanes
-  // whose keys share a digit rarely hit the same LDS word in one atomic
-  uint32_t* hist = hist_all + wave * (kHistCopies * 256);
+  // each wave keeps kHistCopies histograms (lane % kHistCopies picks one) so lanes whose
+  // keys share a digit rarely hit the same LDS word in one atomic
+  constexpr int kHW = hist_words(kHistCopies);
+  uint32_t* hist = hist_all + wave * kHW;
+  uint32_t* const trash = hist + kHistCopies * 256 + lane;
   for (int item = wave; item < nrows * L.n_seg; item += kWaves) {
     const int r = item / L.n_seg;
     const int s = item - r * L.n_seg;
@@ -169,18 +190,31 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
       for (int j = lane; j < T; j += 64) out[j] = j;
       continue;
     }
-    // radix select of the K-th largest key
+    // radix select of the K-th largest key, 8 bits per step from the top.  After a step,
+    // the keys whose fixed bits (pmask) exceed `prefix` are all taken, and `remaining`
+    // more are taken from those equal to it; when that is every one of them, the fixed
+    // bits already decide the selection and the remaining steps are skipped.
     uint32_t prefix = 0, pmask = 0;
-    int remaining = K;   // how many still to take from the elements matching `prefix`
+    int remaining = K;   // how many still to take from the keys matching `prefix`
     for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-      for (int t = 0; t < kHistCopies * 4; ++t) hist[t * 64 + lane] = 0u;
+      for (int t = 0; t < kHW / 64; ++t) hist[t * 64 + lane] = 0u;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      for (int j = lane; j < T; j += 64) {
-        const uint32_t key = row[j];
-        if ((key & pmask) == prefix)
-          atomicAdd(&hist[(lane % kHistCopies) * 256 + ((key >> shift) & 0xFFu)], 1u);
+      // keys in chunks of kChunk per lane: every read of a chunk is issued before the
+      // first one is used, so a step pays the LDS latency once per chunk, not per key
+      for (int base = 0; base < T; base += 64 * kChunk) {
+        uint32_t kc[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+          const int j = base + 64 * u + lane;
+          kc[u] = j < T ? row[j] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+          const bool match = base + 64 * u + lane < T && (kc[u] & pmask) == prefix;
+          atomicAdd(match ? hist + (lane % kHistCopies) * 256 + ((kc[u] >> shift) & 0xFFu) : trash, 1u);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -193,66 +227,90 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(LayerDev L, int R,
         for (int cp = 0; cp < kHistCopies; ++cp) c[t] += hist[cp * 256 + 255 - (lane * 4 + t)];
       }
       const uint32_t local = c[0] + c[1] + c[2] + c[3];
-      uint32_t incl = local;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-      }
+      const uint32_t incl = wave_inclusive_sum(local);
       const uint32_t excl = incl - local;
       // the lane whose range crosses `remaining`
       const bool mine = excl < (uint32_t)remaining && (uint32_t)remaining <= incl;
       const uint64_t bal = __ballot(mine);
       const int owner = bal ? __builtin_ctzll(bal) : 0;
-      uint32_t digit = 0, above = 0;
+      uint32_t digit = 0, above = 0, cnt = 0;
       if (lane == owner) {
         uint32_t acc_above = excl;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (acc_above + c[t] >= (uint32_t)remaining) {
             digit = 255 - (lane * 4 + t);
+            cnt = c[t];
             break;
           }
           acc_above += c[t];
         }
         above = acc_above;
       }
-      digit = __shfl(digit, owner, 64);
-      above = __shfl(above, owner, 64);
+      digit = __builtin_amdgcn_readlane(digit, owner);
+      above = __builtin_amdgcn_readlane(above, owner);
+      cnt = __builtin_amdgcn_readlane(cnt, owner);
       remaining -= (int)above;
       prefix |= digit << shift;
       pmask |= 0xFFu << shift;
       __builtin_amdgcn_wave_barrier();
+      if ((uint32_t)remaining == cnt) break;
     }
-    // prefix is now the K-th largest key; keep all keys above it and the first
-    // `remaining` keys equal to it, in ascending tile order
-    const uint32_t thr = prefix;
+    // keep every key whose fixed bits exceed `prefix` and the first `remaining` keys whose
+    // fixed bits equal it, in ascending tile order
     int taken = 0, eq_seen = 0;
-    for (int base = 0; base < T && taken < K; base += 64) {
-      const int j = base + lane;
-      const uint32_t key = j < T ? row[j] : 0u;
-      const bool gt = j < T && key > thr;
-      const bool eq = j < T && key == thr;
-      const uint64_t beq = __ballot(eq);
-      const int eq_rank = eq_seen + prefix_below(beq);
-      const bool take = gt || (eq && eq_rank < remaining);
-      const uint64_t bt = __ballot(take);
-      const int pos = taken + prefix_below(bt);
-      if (take && pos < K) out[pos] = j;
-      taken += __popcll(bt);
-      eq_seen += __popcll(beq);
+    for (int base = 0; base < T && taken < K; base += 64 * kChunk) {
+      uint32_t kc[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int j = base + 64 * u + lane;
+        kc[u] = j < T ? row[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int j = base + 64 * u + lane;
+        const uint32_t fixed = kc[u] & pmask;
+        const bool gt = j < T && fixed > prefix;
+        const bool eq = j < T && fixed == prefix;
+        const uint64_t beq = __ballot(eq);
+        const int eq_rank = eq_seen + prefix_below(beq);
+        const bool take = gt || (eq && eq_rank < remaining);
+        const uint64_t bt = __ballot(take);
+        const int pos = taken + prefix_below(bt);
+        if (take && pos < K) out[pos] = j;
+        taken += __popcll(bt);
+        eq_seen += __popcll(beq);
+      }
     }
   }
 }
 
+// Waves per workgroup and histogram copies per wave for a predictor width: 16 waves (so
+// that one workgroup works on 16 rows at once and hides the latency of each row's serial
+// radix steps) where the kernel's registers allow it, fewer for wide predictors.
+template <int kMaxKSteps>
+struct TopkShape {
+  static constexpr int waves = kMaxKSteps <= 2 ? 16 : kMaxKSteps <= 4 ? 8 : 4;
+  static constexpr int copies = kMaxKSteps <= 2 ? 1 : 4;
+};
+
 }  // namespace
 
-int score_rows_per_block(int Tk) {
+// LDS bytes of one workgroup's histograms for a predictor width p
+static int hist_bytes(int p) {
+  auto f = [](auto shape) { return shape.waves * hist_words(shape.copies) * 4; };
+  if (p <= 64) return f(TopkShape<2>{});
+  if (p <= 128) return f(TopkShape<4>{});
+  if (p <= 256) return f(TopkShape<8>{});
+  return f(TopkShape<12>{});
+}
+
+int score_rows_per_block(int Tk, int p) {
   // Prefer a block that lets two workgroups share a CU (<= 78 KB of LDS each); fall
-  // back to one workgroup per CU with up to 144 KB when fewer than 8 rows would fit.
-  const int hist = kWaves * kHistCopies * 256 * 4;
+  // back to one workgroup per CU with up to 150 KB when fewer than 8 rows would fit.
+  const int hist = hist_bytes(p);
   int r = (78 * 1024 - hist) / (Tk * 4);
-  if (r < 8) r = (144 * 1024 - hist) / (Tk * 4);
+  if (r < 8) r = (150 * 1024 - hist) / (Tk * 4);
   if (r > 16) r = 16;
   if (r < 1) r = 1;
   return r;
@@ -260,28 +318,29 @@ int score_rows_per_block(int Tk) {
 
 hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float* k_hat,
                              int32_t* idx, float* scores, hipStream_t s) {
-  const int R = score_rows_per_block(L.Tk);
-  const size_t lds = (size_t)R * L.Tk * 4 + kWaves * kHistCopies * 256 * 4;
+  const int R = score_rows_per_block(L.Tk, L.p);
+  const size_t lds = (size_t)R * L.Tk * 4 + hist_bytes(L.p);
   dim3 grid((unsigned)((L.Tq + R - 1) / R), (unsigned)L.H, (unsigned)L.B);
   // the kernel is instantiated for 32-wide predictor steps: p <= 64, 128, 256, 384
-  auto run = [&](auto kern) -> hipError_t {
+  auto run = [&](auto kern, int waves) -> hipError_t {
     if (lds > 64 * 1024) {
       hipError_t e = hipFuncSetAttribute((const void*)kern,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, L, R, q_hat, k_hat, idx, scores);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, s, L, R, q_hat, k_hat, idx, scores);
     return hipSuccess;
   };
+  auto go = [&](auto shape, auto kern) { return run(kern, decltype(shape)::waves); };
   hipError_t e;
   if (L.p <= 64)
-    e = run(score_topk_kernel<2>);
+    e = go(TopkShape<2>{}, score_topk_kernel<2, TopkShape<2>::waves, TopkShape<2>::copies>);
   else if (L.p <= 128)
-    e = run(score_topk_kernel<4>);
+    e = go(TopkShape<4>{}, score_topk_kernel<4, TopkShape<4>::waves, TopkShape<4>::copies>);
   else if (L.p <= 256)
-    e = run(score_topk_kernel<8>);
+    e = go(TopkShape<8>{}, score_topk_kernel<8, TopkShape<8>::waves, TopkShape<8>::copies>);
   else
-    e = run(score_topk_kernel<12>);
+    e = go(TopkShape<12>{}, score_topk_kernel<12, TopkShape<12>::waves, TopkShape<12>::copies>);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

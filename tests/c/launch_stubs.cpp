@@ -203,6 +203,6 @@ hipError_t launch_window_indices(int64_t q0, int64_t qlen, int64_t tile, int64_t
   return done();
 }
 
-int score_rows_per_block(int) { return 1; }
+int score_rows_per_block(int, int) { return 1; }
 
 }  // namespace veda
