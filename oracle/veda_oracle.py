@@ -287,10 +287,11 @@ def attend_rows(q_rows: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
 
 def attend_tile(q_bits, k_bits, v_bits, b: int, h: int, qtile: int, idx_row: np.ndarray,
                 tile: int, query: Tuple[int, int], segments, dense,
-                scale: Optional[float] = None, dq=bf16_bits_to_f64, dk=bf16_bits_to_f64):
+                scale: Optional[float] = None, dq=bf16_bits_to_f64, dk=bf16_bits_to_f64,
+                dv=bf16_bits_to_f64):
     """O7 for one (batch, head, query tile): returns (out [t, d], lse [t]) in float64.
-    dq / dk turn stored Q / K elements into values (bf16 bits by default; fp8_values for
-    E4M3FN codes)."""
+    dq / dk / dv turn stored Q / K / V elements into values (bf16 bits by default;
+    fp8_values for E4M3FN codes)."""
     d = q_bits.shape[3]
     if scale is None or scale == 0.0:
         scale = 1.0 / math.sqrt(d)
@@ -301,7 +302,7 @@ def attend_tile(q_bits, k_bits, v_bits, b: int, h: int, qtile: int, idx_row: np.
         raise ValueError("query tile attends to no keys")
     qr = dq(q_bits[b, q0:q1, h, :])
     kr = dk(k_bits[b, toks, h, :])
-    vr = bf16_bits_to_f64(v_bits[b, toks, h, :])
+    vr = dv(v_bits[b, toks, h, :])
     return attend_rows(qr, kr, vr, scale)
 
 
@@ -324,9 +325,9 @@ def attend_all_keys(q_bits, k_bits, v_bits, b: int, h: int, rows: Tuple[int, int
 def attend(q_bits, k_bits, v_bits, idx: np.ndarray, tile: int, query: Tuple[int, int],
            segments, dense, scale: Optional[float] = None,
            pairs: Optional[Iterable[Tuple[int, int, int]]] = None,
-           dq=bf16_bits_to_f64, dk=bf16_bits_to_f64):
-    """O7 over a layer, or over the (b, h, query tile) triples in `pairs` (dq / dk as in
-    attend_tile).
+           dq=bf16_bits_to_f64, dk=bf16_bits_to_f64, dv=bf16_bits_to_f64):
+    """O7 over a layer, or over the (b, h, query tile) triples in `pairs` (dq / dk / dv as
+    in attend_tile).
 
     Returns dict {(b, h, qtile): (out [t, d], lse [t])}.
     """
@@ -337,7 +338,7 @@ def attend(q_bits, k_bits, v_bits, idx: np.ndarray, tile: int, query: Tuple[int,
     res = {}
     for (b, h, i) in pairs:
         res[(b, h, i)] = attend_tile(q_bits, k_bits, v_bits, b, h, i, idx[b, h, i], tile,
-                                     query, segments, dense, scale, dq, dk)
+                                     query, segments, dense, scale, dq, dk, dv)
     return res
 
 

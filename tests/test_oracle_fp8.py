@@ -108,3 +108,30 @@ def test_fp8_attention_equals_bf16_attention_on_the_decoded_values():
     b = O.attend(qb, kb, v, idx, tile, query, segs, dense)
     for key in a:
         assert np.array_equal(a[key][0], b[key][0]) and np.array_equal(a[key][1], b[key][1])
+
+
+def test_fp8_v_attention_equals_bf16_attention_on_the_decoded_values():
+    """V given as E4M3FN codes (per-tensor scale) through the dv decoder is the bf16
+    attention (pinned against SDPA) on the decoded V, which is exact in bf16."""
+    g = np.random.default_rng(8)
+    B, N, H, d, tile = 1, 200, 2, 64, 64
+    q, k, v = (I.f32_to_bf16_bits(3.0 * g.standard_normal((B, N, H, d)).astype(np.float32)) for _ in range(3))
+    q8, eq = O.quantize_fp8(q)
+    k8, ek = O.quantize_fp8(k)
+    v8, ev = O.quantize_fp8(v)
+    assert ev != 0 or np.abs(O.bf16_bits_to_f64(v)).max() <= 448
+    qb, kb, vb = (O.f64_to_bf16_bits_rne(O.dequant_e4m3fn(c, e)) for c, e in ((q8, eq), (k8, ek), (v8, ev)))
+    segs = [(0, 160, 2)]
+    dense = [(160, 40)]
+    query = (0, 160)
+    idx = np.array([[[[0, 2], [1, 2], [0, 1]] for _ in range(H)]], dtype=np.int32)
+    a = O.attend(q8, k8, v8, idx, tile, query, segs, dense, dq=O.fp8_values(eq), dk=O.fp8_values(ek),
+                 dv=O.fp8_values(ev))
+    b = O.attend(qb, kb, vb, idx, tile, query, segs, dense)
+    for key in a:
+        assert np.array_equal(a[key][0], b[key][0]) and np.array_equal(a[key][1], b[key][1])
+    # and the decoded V differs from V by at most E4M3's half step (2^-4 relative, or
+    # 2^-10 * 2^e absolute below the normal range)
+    vv = O.bf16_bits_to_f64(v)
+    dec = O.dequant_e4m3fn(v8, ev)
+    assert np.all(np.abs(dec - vv) <= np.maximum(2.0 ** -4 * np.abs(vv), 2.0 ** (-10 + ev)) + 1e-300)
