@@ -48,7 +48,7 @@ def parse(argv=None):
     ap.add_argument("--no-patterns", action="store_true",
                     help="skip the budget 16/32/64 and VDN window timings (field 'patterns')")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the FP8 Q.K^T path timing (field 'fp8qk')")
+                    help="skip the FP8 paths' timing (fields 'fp8qk' and 'fp8')")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (byte-counter calibration)")
     ap.add_argument("--seed", type=int, default=None,
@@ -457,50 +457,76 @@ def random_pattern(lay, kernel_reps, log):
             "actual_tflops_attn": round(fl / (med * 1e-3) / 1e12, 1)}
 
 
-def measure_fp8qk(lay, kernel_reps, log):
-    """The FP8 Q.K^T path on the same layer and index sets: Q and K quantised on the GPU
-    (E4M3FN, per-tensor power-of-two scale), then veda_sparse_attn_fp8qk.  Its first
-    product runs at the FP8 matrix rate and its second at the bf16 rate, so the peak it is
-    compared with is the harmonic mean of the two (equal flops in each product)."""
+def measure_fp8(lay, kernel_reps, log):
+    """The two FP8 paths on the same layer and index sets, Q and K quantised on the GPU
+    (E4M3FN, per-tensor power-of-two scale):
+      * fp8qk: veda_sparse_attn_fp8qk, FP8 first product, bf16 P.V.  Its peak is the
+        harmonic mean of the FP8 and bf16 rates (equal flops in each product);
+      * fp8: veda_sparse_attn_fp8, V quantised to the blocked FP8 layout and P rounded to
+        E4M3FN, both products at the FP8 rate."""
     import torch
     B, wl = lay.B, lay.wl
     q8, qs = B.quantize_fp8(lay.L, lay.qd)
     k8, ks = B.quantize_fp8(lay.L, lay.kd)
+    vt, vs = B.quantize_fp8_vt(lay.L, lay.vd)
     out8 = torch.zeros_like(lay.qd)
+    out8v = torch.zeros_like(lay.qd)
 
     def quant():
         B.quantize_fp8(lay.L, lay.qd, out=q8, scale=qs)
         B.quantize_fp8(lay.L, lay.kd, out=k8, scale=ks)
 
+    def quant_v():
+        B.quantize_fp8_vt(lay.L, lay.vd, out=vt, scale=vs)
+
     def attn8():
         B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, lay.idx, lay.dense, out=out8)
+
+    def attn8v():
+        B.sparse_attn_fp8(lay.L, q8, k8, vt, qs, ks, vs, lay.idx, lay.dense, out=out8v)
 
     lay.select()
     lay.attn()
     quant()
+    quant_v()
     attn8()
+    attn8v()
     torch.cuda.synchronize()
     q_ms, _, q_med = time_events(quant, kernel_reps)
+    qv_ms, _, qv_med = time_events(quant_v, kernel_reps)
     a_ms, a_min, a_med = time_events(attn8, kernel_reps)
+    v_ms, v_min, v_med = time_events(attn8v, kernel_reps)
     fl = lay.actual_flops(lay.idx.cpu().numpy())
     q0, q1 = wl.query.start, wl.query.start + wl.query.length
     diff = (out8[:, q0:q1].float() - lay.out[:, q0:q1].float()).abs()
+    diffv = (out8v[:, q0:q1].float() - lay.out[:, q0:q1].float()).abs()
     mixed_peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
     tf = fl / (a_med * 1e-3) / 1e12
+    tfv = fl / (v_med * 1e-3) / 1e12
     log(f"[{wl.name}] fp8 Q.K^T attention: {a_med:.3f} ms ({tf:.0f} TFLOP/s), quantising Q and K {q_med:.3f} ms")
+    log(f"[{wl.name}] fp8 Q.K^T + P.V attention: {v_med:.3f} ms ({tfv:.0f} TFLOP/s), quantising V {qv_med:.3f} ms")
     res = {"attn_ms": round(a_ms, 4), "attn_ms_median": round(a_med, 4), "attn_ms_min": round(a_min, 4),
            "quantize_qk_ms": round(q_med, 4), "actual_tflops_attn": round(tf, 1),
            "mixed_peak_tflops": round(mixed_peak, 1), "frac_mixed_peak": round(tf / mixed_peak, 4),
            "speedup_vs_bf16_attn": None,
            "max_abs_vs_bf16_out": round(float(diff.max()), 5), "mean_abs_vs_bf16_out": round(float(diff.mean()), 6),
            "kernel": f"sparse_attn_fp8qk_pingpong_kernel<{wl.d}>"}
-    del out8
+    resv = {"attn_ms": round(v_ms, 4), "attn_ms_median": round(v_med, 4), "attn_ms_min": round(v_min, 4),
+            "quantize_qk_ms": round(q_med, 4), "quantize_v_ms": round(qv_med, 4),
+            "actual_tflops_attn": round(tfv, 1), "peak_tflops": PEAK_FP8_TFLOPS,
+            "frac_fp8_peak": round(tfv / PEAK_FP8_TFLOPS, 4), "speedup_vs_bf16_attn": None,
+            "speedup_vs_fp8qk_attn": round(a_med / v_med, 3),
+            "max_abs_vs_bf16_out": round(float(diffv.max()), 5),
+            "mean_abs_vs_bf16_out": round(float(diffv.mean()), 6),
+            "kernel": f"sparse_attn_fp8_pingpong_kernel<{wl.d}>"}
+    del out8, out8v
 
     def attn8_with(idx):
-        """FP8 Q.K^T attention of this layer with the given index sets (for the parity leg)."""
-        return B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, idx, lay.dense)
+        """Both FP8 paths of this layer with the given index sets (for the parity leg)."""
+        return {"fp8qk": B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, idx, lay.dense),
+                "fp8": B.sparse_attn_fp8(lay.L, q8, k8, vt, qs, ks, vs, idx, lay.dense)}
 
-    return res, attn8_with
+    return res, resv, attn8_with
 
 
 def sdpa_dense(lay, reps, log):
@@ -609,13 +635,13 @@ def cpu_baseline(lay, log, budget_s=20.0, attn8_with=None):
     # GPU attention fed the oracle's index sets (and the FP8 Q.K^T path, if given, likewise)
     idx_ref_dev = torch.from_numpy(idx_ref).to(lay.qd.device)
     out_gpu = lay.B.sparse_attn(lay.L, lay.qd, lay.kd, lay.vd, idx_ref_dev, lay.dense)
-    out8 = attn8_with(idx_ref_dev) if attn8_with is not None else None
+    out8 = attn8_with(idx_ref_dev) if attn8_with is not None else {}
     del idx_ref_dev
     torch.cuda.synchronize()
     # oracle attention on random (head, tile) pairs until the budget is used
     rng = np.random.default_rng(0)
     pairs, t_att = [], 0.0
-    diffs, diffs8 = [], []
+    diffs, diffs8 = [], {name: [] for name in out8}
     Tq = wl.n_query_tiles
     while t_att < budget_s * 2 / 3 and len(pairs) < wl.B * wl.H * Tq:
         pr = (int(rng.integers(0, wl.B)), int(rng.integers(0, wl.H)), int(rng.integers(0, Tq)))
@@ -627,9 +653,9 @@ def cpu_baseline(lay, log, budget_s=20.0, attn8_with=None):
         r0 = wl.query.start + pr[2] * wl.tile
         got = out_gpu[pr[0], r0:r0 + ref.shape[0], pr[1]].to(torch.float64).cpu().numpy()
         diffs.append(np.abs(got - ref).ravel())
-        if out8 is not None:
-            got8 = out8[pr[0], r0:r0 + ref.shape[0], pr[1]].to(torch.float64).cpu().numpy()
-            diffs8.append(np.abs(got8 - ref).ravel())
+        for name, o8 in out8.items():
+            got8 = o8[pr[0], r0:r0 + ref.shape[0], pr[1]].to(torch.float64).cpu().numpy()
+            diffs8[name].append(np.abs(got8 - ref).ravel())
     del out_gpu, out8
     d = np.concatenate(diffs)
     log(f"[cpu] oracle attention on {len(pairs)} (head, tile) pairs")
@@ -653,12 +679,15 @@ def cpu_baseline(lay, log, budget_s=20.0, attn8_with=None):
         "what": ("GPU selection of every head and row against the oracle's (scores, index sets); GPU attention "
                  "fed the oracle's index sets against the oracle on the sampled (head, query tile) pairs"),
     }
-    if diffs8:
-        d8 = np.concatenate(diffs8)
-        parity["fp8qk_vs_oracle"] = {
-            "max_abs": float(d8.max()), "mean_abs": float(d8.mean()), "pairs": len(pairs),
-            "what": ("FP8 Q.K^T attention (Q, K quantised to E4M3FN) against the fp64 oracle of the bf16 "
-                     "inputs on the same pairs: the error of FP8 logits, outside the bf16 attention bar")}
+    what8 = {"fp8qk": ("FP8 Q.K^T attention (Q, K quantised to E4M3FN) against the fp64 oracle of the bf16 "
+                       "inputs on the same pairs: the error of FP8 logits, outside the bf16 attention bar"),
+             "fp8": ("FP8 attention (Q, K, V quantised to E4M3FN, P rounded to E4M3FN) against the fp64 "
+                     "oracle of the bf16 inputs on the same pairs: the error of the FP8 formats, outside "
+                     "the bf16 attention bar")}
+    for name, ds in diffs8.items():
+        d8 = np.concatenate(ds)
+        parity[f"{name}_vs_oracle"] = {"max_abs": float(d8.max()), "mean_abs": float(d8.mean()),
+                                       "pairs": len(pairs), "what": what8[name]}
     log(f"[cpu] parity: {parity}")
     return {
         "value": lay.dense_flops() / layer_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
@@ -725,10 +754,11 @@ def main():
     patterns = None if args.no_patterns else measure_patterns(lay, args.kernel_reps, log)
     if patterns is not None:
         patterns["random_indices"] = random_pattern(lay, args.kernel_reps, log)
-    fp8qk, attn8_with = None, None
+    fp8qk, fp8, attn8_with = None, None, None
     if not args.no_fp8 and lay.wl.tile == 128:
-        fp8qk, attn8_with = measure_fp8qk(lay, args.kernel_reps, log)
+        fp8qk, fp8, attn8_with = measure_fp8(lay, args.kernel_reps, log)
         fp8qk["speedup_vs_bf16_attn"] = round(res["attn_ms_median"] / fp8qk["attn_ms_median"], 3)
+        fp8["speedup_vs_bf16_attn"] = round(res["attn_ms_median"] / fp8["attn_ms_median"], 3)
     peaks = device_peaks(log)
     also = None
     if args.also and args.also != "none" and args.also != args.workload:
@@ -756,6 +786,8 @@ def main():
         cpu, parity = cpu_baseline(lay, log, attn8_with=attn8_with)
         if fp8qk is not None and "fp8qk_vs_oracle" in parity:
             fp8qk["vs_oracle_bf16_inputs"] = parity.pop("fp8qk_vs_oracle")
+        if fp8 is not None and "fp8_vs_oracle" in parity:
+            fp8["vs_oracle_bf16_inputs"] = parity.pop("fp8_vs_oracle")
     attn8_with = None
     torch.cuda.empty_cache()
     achieved = res["actual_tflops_attn"]
@@ -813,6 +845,7 @@ def main():
         "parity": parity,
         "patterns": patterns,
         "fp8qk": fp8qk,
+        "fp8": fp8,
         "also": also,
         "sweep": sweep,
         "detail": res,

@@ -93,6 +93,10 @@ def _load():
         "veda_sparse_attn_fp8qk": (ctypes.c_int, [L, P, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                                   ctypes.c_float, P, P, P]),
         "veda_quantize_fp8_e4m3": (ctypes.c_int, [L, P, P, P, P]),
+        "veda_sparse_attn_fp8": (ctypes.c_int, [L, P, P, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+                                                ctypes.c_float, P, P, P]),
+        "veda_quantize_fp8_e4m3_vt": (ctypes.c_int, [L, P, P, P, P]),
+        "veda_fp8_vt_bytes": (ctypes.c_size_t, [L]),
         "veda_sparse_attn_check": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                                   ctypes.c_float, P]),
         "veda_layer_attn": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
@@ -134,11 +138,12 @@ def exported_symbols():
                         "veda_st_open", "veda_st_close", "veda_st_count", "veda_st_info",
                         "veda_st_find", "veda_st_read", "veda_st_metadata_count",
                         "veda_st_metadata_at", "veda_sparse_attn_fp8qk",
-                        "veda_quantize_fp8_e4m3")]
+                        "veda_quantize_fp8_e4m3", "veda_sparse_attn_fp8", "veda_quantize_fp8_e4m3_vt",
+                        "veda_fp8_vt_bytes")]
 
 
 # VEDA_ABI_VERSION of include/veda.h that this binding marshals for
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 def abi_version() -> int:
@@ -393,6 +398,61 @@ def sparse_attn_fp8qk(layer: Layer, q8, k8, v, q_scale, k_scale, idx, dense: Seq
                                         _ptr(k_scale), _ptr(idx), arr, n, float(scale), _ptr(out), _ptr(lse),
                                         _stream(stream))
     _check(st, "veda_sparse_attn_fp8qk")
+    return (out, lse) if want_lse else out
+
+
+def fp8_vt_bytes(layer: Layer) -> int:
+    """Bytes of the blocked FP8 V that quantize_fp8_vt writes (0: layer not supported)."""
+    return int(_load().veda_fp8_vt_bytes(ctypes.byref(layer)))
+
+
+def _check_vt(layer: Layer, vt):
+    n = fp8_vt_bytes(layer)
+    if n == 0:
+        raise ValueError("layer not supported by the FP8-V layout")
+    if vt.dtype != torch.uint8 or not vt.is_cuda or not vt.is_contiguous() or vt.numel() != n:
+        raise ValueError(f"vt must be a contiguous uint8 device tensor of {n} bytes")
+
+
+def quantize_fp8_vt(layer: Layer, v, out=None, scale=None, stream=None):
+    """bf16 V -> (E4M3FN codes in d-major 64-token blocks, uint8 [B, H, ceil(N / 64), d, 64]
+    with the chunk permutation of veda_quantize_fp8_e4m3_vt; float32 [1] scale 2^e)."""
+    _check_qkv(layer, v)
+    if out is None:
+        out = torch.empty((layer.B, layer.H, -(-layer.n_tokens // 64), layer.d, 64), dtype=torch.uint8,
+                          device=v.device)
+    _check_vt(layer, out)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=v.device)
+    _check_scale(scale)
+    st = _load().veda_quantize_fp8_e4m3_vt(ctypes.byref(layer), _ptr(v), _ptr(out), _ptr(scale), _stream(stream))
+    _check(st, "veda_quantize_fp8_e4m3_vt")
+    return out, scale
+
+
+def sparse_attn_fp8(layer: Layer, q8, k8, vt, q_scale, k_scale, v_scale, idx,
+                    dense: Sequence[Tuple[int, int]] = (), scale: float = 0.0, out=None, want_lse: bool = False,
+                    stream=None):
+    """veda_sparse_attn with E4M3FN Q, K (as quantize_fp8 returns them), V in the blocked layout
+    of quantize_fp8_vt, and P rounded to E4M3FN.  Returns out (bf16, q8's shape and strides)
+    [and lse fp32 [B, H, query.len]]."""
+    _check_fp8(layer, q8, k8)
+    _check_vt(layer, vt)
+    _check_scale(q_scale, k_scale, v_scale)
+    if out is None:
+        out = torch.empty_strided(tuple(q8.shape), tuple(q8.stride()), dtype=torch.bfloat16,
+                                  device=q8.device).zero_()
+    else:
+        _check_qkv(layer, out)
+    lse = torch.empty((layer.B, layer.H, layer.query.len), dtype=torch.float32, device=q8.device) \
+        if want_lse else None
+    if idx is not None:
+        _check_idx(layer, idx, q8.device)
+    arr, n = dense_ranges(list(dense))
+    st = _load().veda_sparse_attn_fp8(ctypes.byref(layer), _ptr(q8), _ptr(k8), _ptr(vt), _ptr(q_scale),
+                                      _ptr(k_scale), _ptr(v_scale), _ptr(idx), arr, n, float(scale), _ptr(out),
+                                      _ptr(lse), _stream(stream))
+    _check(st, "veda_sparse_attn_fp8")
     return (out, lse) if want_lse else out
 
 

@@ -295,6 +295,53 @@ int veda_quantize_fp8_e4m3(const veda_layer* layer, const void* x, uint8_t* x8, 
   return hip_status(veda::launch_quantize_fp8(D, layer->n_tokens, x, x8, scale, (hipStream_t)stream));
 }
 
+size_t veda_fp8_vt_bytes(const veda_layer* layer) {
+  if (check_layer(layer, false) != VEDA_OK) return 0;
+  const int64_t blocks = ceil_div(layer->n_tokens, 64);
+  const int64_t bh = (int64_t)layer->B * layer->H;
+  if (blocks > INT32_MAX / bh) return 0;   // the quantiser runs one workgroup per block
+  return (size_t)(bh * blocks) * (size_t)layer->d * 64u;
+}
+
+int veda_quantize_fp8_e4m3_vt(const veda_layer* layer, const void* v, uint8_t* vt, float* v_scale,
+                              void* stream) {
+  int st = check_layer(layer, false);
+  if (st != VEDA_OK) return st;
+  if (!v || !vt || !v_scale) return VEDA_EINVAL;
+  if (!aligned16(v) || !aligned16(vt) || (reinterpret_cast<uintptr_t>(v_scale) & 3u)) return VEDA_EINVAL;
+  if (veda_fp8_vt_bytes(layer) == 0) return VEDA_EUNSUPPORTED;
+  LayerDev D = to_dev(layer);
+  return hip_status(veda::launch_quantize_fp8_vt(D, layer->n_tokens, v, vt, v_scale, (hipStream_t)stream));
+}
+
+int veda_sparse_attn_fp8(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const uint8_t* vt,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
+                         void* out, float* lse_opt, void* stream) {
+  veda::DenseDev DD{};
+  int st = sparse_attn_check(layer, q8, k8, vt, idx, dense, n_dense, scale, out, &DD);
+  if (st != VEDA_OK) return st;
+  if (!q_scale || !k_scale || !v_scale) return VEDA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+    return VEDA_EINVAL;
+  if ((layer->stride_b % 16) || (layer->stride_n % 16) || (layer->stride_h % 16)) return VEDA_EINVAL;
+  if (lse_opt && !aligned16(lse_opt)) return VEDA_EINVAL;
+  if (layer->tile != 128) return VEDA_EUNSUPPORTED;
+  // every key block starts a 64-token block of vt
+  for (int s = 0; s < layer->n_seg; ++s)
+    if (layer->seg[s].start % 64) return VEDA_EUNSUPPORTED;
+  for (int i = 0; i < DD.n; ++i)
+    if (DD.r[i].start % 64) return VEDA_EUNSUPPORTED;
+  if (veda_fp8_vt_bytes(layer) == 0) return VEDA_EUNSUPPORTED;
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) return VEDA_OK;
+  if (!veda::two_group_fits(D, DD)) return VEDA_EUNSUPPORTED;
+  if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
+  return hip_status(veda::launch_sparse_attn_fp8(D, DD, q8, k8, vt, layer->n_tokens, idx, scale, q_scale,
+                                                 k_scale, v_scale, out, lse_opt, (hipStream_t)stream));
+}
+
 int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
                     const void* wq, const void* wk, const veda_range* dense, int32_t n_dense,
                     const veda_range* dense_queries, int32_t n_dense_queries, float scale,

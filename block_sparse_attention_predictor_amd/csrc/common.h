@@ -62,6 +62,18 @@ hipError_t launch_quantize_fp8(const LayerDev& L, int64_t n_tokens, const void* 
                                 float* scale, hipStream_t s);
 hipError_t launch_dequant_e4m3(const uint8_t* src, void* dst, int64_t n, int32_t pow2_exp,
                                hipStream_t s);
+// bf16 V [B, n_tokens, H, d] (layer strides) -> E4M3FN codes in d-major blocks of 64 tokens
+// ([B, H, ceil(n_tokens / 64), d, 64], chunk-swizzled; see dequant.hip), per-tensor scale
+// as launch_quantize_fp8.
+hipError_t launch_quantize_fp8_vt(const LayerDev& L, int64_t n_tokens, const void* v, uint8_t* vt,
+                                  float* scale, hipStream_t s);
+// FP8 Q, K (as launch_sparse_attn_fp8qk) and V in the blocked layout above; P rounded to
+// E4M3FN for the second product.  Needs 128-row tiles, block starts on multiples of 64 and
+// a block list within the two-group kernel's table.
+hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& D, const void* q8, const void* k8,
+                                  const void* vt, int64_t n_tokens, const int32_t* idx, float scale,
+                                  const float* q_scale, const float* k_scale, const float* v_scale, void* out,
+                                  float* lse, hipStream_t s);
 
 // Teacher block attention mass (two launches: dense lse, then per-tile mass) and the
 // recall of an index set under it (see block_mass.hip).  L must carry full budgets.

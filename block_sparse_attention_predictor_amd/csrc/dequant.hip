@@ -153,7 +153,79 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(LayerDev L, int64_t n
   });
 }
 
+// V for the FP8 attention's second product, d-major in blocks of 64 tokens: block
+// (b, h, g) is d rows of 64 bytes, row c holding the codes of V[b, 64 g + t, h, c] for
+// t = 0..63 (zeros past the last token), its four 16-byte chunks XOR-swizzled by
+// (c >> 1) & 3 so that the kernel's operand reads (eight consecutive rows, one chunk
+// each) hit distinct LDS banks.  One workgroup quantises one block through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void fp8_quantize_vt_kernel(LayerDev L, int64_t n_tokens, int64_t n_blocks,
+                                                               const uint16_t* __restrict__ x,
+                                                               uint8_t* __restrict__ vt,
+                                                               const float* __restrict__ scale) {
+  __shared__ uint8_t tile[64][D + 4];           // token-major codes of the block
+  int ex;
+  frexpf(scale[0], &ex);
+  const int e = ex - 1;                          // scale = 2^e
+  const int64_t blk = blockIdx.x;
+  const int64_t g = blk % n_blocks;
+  const int64_t bh = blk / n_blocks;
+  const int64_t h = bh % L.H, b = bh / L.H;
+  constexpr int VPR = D / 8;                     // 8-element vectors per token row
+  for (int u = threadIdx.x; u < 64 * VPR; u += 256) {
+    const int t = u / VPR, c8 = u % VPR;
+    const int64_t n = 64 * g + t;
+    uint32_t c[2] = {0u, 0u};
+    if (n < n_tokens) {
+      const uint4 w = *reinterpret_cast<const uint4*>(x + b * L.sb + n * L.sn + h * L.sh + 8 * c8);
+      const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = e4m3_code(ldexpf(__uint_as_float(a[i] << 16), -e));
+        const uint32_t hi = e4m3_code(ldexpf(__uint_as_float(a[i] & 0xFFFF0000u), -e));
+        c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+      }
+    }
+    *reinterpret_cast<uint32_t*>(&tile[t][8 * c8]) = c[0];
+    *reinterpret_cast<uint32_t*>(&tile[t][8 * c8 + 4]) = c[1];
+  }
+  __syncthreads();
+  uint8_t* const dst = vt + blk * (int64_t)(D * 64);
+  for (int u = threadIdx.x; u < D * 4; u += 256) {
+    const int c = u >> 2, pc = u & 3;
+    const int lc = pc ^ ((c >> 1) & 3);          // logical chunk: tokens 16 lc .. 16 lc + 15
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t0 = 16 * lc + 4 * q;
+      w[q] = (uint32_t)tile[t0][c] | ((uint32_t)tile[t0 + 1][c] << 8) | ((uint32_t)tile[t0 + 2][c] << 16) |
+             ((uint32_t)tile[t0 + 3][c] << 24);
+    }
+    *reinterpret_cast<uint4*>(dst + c * 64 + pc * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_fp8_vt(const LayerDev& L, int64_t n_tokens, const void* v, uint8_t* vt,
+                                  float* scale, hipStream_t s) {
+  const int64_t amax_blocks = std::min<int64_t>((int64_t)L.B * n_tokens, 8192);
+  const int64_t n_blocks = (n_tokens + 63) / 64;
+  const int64_t grid = (int64_t)L.B * L.H * n_blocks;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  uint32_t* word = reinterpret_cast<uint32_t*>(scale);
+  auto xx = static_cast<const uint16_t*>(v);
+  hipLaunchKernelGGL(fp8_clear_kernel, dim3(1), dim3(1), 0, s, word);
+  hipLaunchKernelGGL(fp8_amax_kernel, dim3((unsigned)amax_blocks), dim3(256), 0, s, L, n_tokens, xx, word);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(1), 0, s, word);
+  if (L.d == 128)
+    hipLaunchKernelGGL((fp8_quantize_vt_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, L, n_tokens, n_blocks,
+                       xx, vt, scale);
+  else
+    hipLaunchKernelGGL((fp8_quantize_vt_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, L, n_tokens, n_blocks,
+                       xx, vt, scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant_e4m3(const uint8_t* src, void* dst, int64_t n, int32_t pow2_exp,
                                hipStream_t s) {

@@ -67,6 +67,11 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32_t;
 
 constexpr int KB = 64;            // keys per block (the single-pipeline kernel also runs 32)
 constexpr float kLazySum = 256.0f;   // largest per-lane weight sum kept against a stale maximum
+// FP8 weights: 2^(x + kW8Shift) for exponents x (against the running maximum) up to kW8Lazy,
+// so every weight stays below 2^8.5 < 448 and weights down to 2^-13 of the row maximum
+// still round to a nonzero code (the smallest subnormal E4M3 value is 2^-9)
+constexpr float kW8Shift = 4.0f;
+constexpr float kW8Lazy = 4.5f;
 
 struct Block {
   int64_t start;
@@ -522,14 +527,26 @@ __device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseD
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales); V, P and the second product stay
 // bf16.  A K row is then d bytes: the K stages use the first half of their space, a
 // block's K DMA is half as many loads, and S^T takes 2 * d / 64 products instead of d / 8.
-template <int D, bool K8, bool T2>
+//
+// V8 (with K8): V is FP8 too, in d-major blocks of 64 tokens (one 8 KB DMA per block,
+// see the V quantiser), and P is rounded to E4M3FN for the second product, also on the
+// f8f6f4 matrix cores: O^T += V^T . P^T, A = V^T rows straight from LDS, B = P^T packed
+// from S^T's accumulators.  For that, S^T's K operand rows are read in a permuted order:
+// accumulator row 8 g + 4 h + t of the 32-row tile mb holds key 32 h + 16 mb + 4 g + t, so
+// the 32 weights a lane holds are keys 32 h .. 32 h + 31 in order, which is the B
+// operand's layout.  The row sums come from one more product with an all-ones A operand,
+// so the normaliser is the sum of exactly the rounded weights the numerator used.  The
+// weights are 2^(x + kW8Shift) for exponents x against the running maximum, kept while no
+// x exceeds kW8Lazy (every weight < 2^8.5, inside E4M3's range of 448).
+template <int D, bool K8, bool T2, bool V8 = false>
 __device__ __forceinline__ void pingpong_attn(
     const LayerDev& L, const DenseDev& DN, const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ q,
-    const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ k, const uint16_t* __restrict__ v,
+    const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    int by_heads) {
+    int by_heads, int64_t vt_head_bytes = 0, float out_scale = 1.0f) {
   using KT = std::conditional_t<K8, uint8_t, uint16_t>;
   static_assert(!(K8 && T2), "the FP8 form runs 128-row tiles only");
+  static_assert(!V8 || K8, "FP8 V needs FP8 Q and K");
   constexpr int NW = 4;                       // waves per group
   constexpr int KBK = T2 ? 32 : KB;           // keys per block
   constexpr int MB = KBK / 32;                // 32-key S^T tiles per block
@@ -538,7 +555,7 @@ __device__ __forceinline__ void pingpong_attn(
   constexpr int TS = 64 * WS;                 // threads per stream
   constexpr int CAP = T2 ? kTabCap / 2 : kTabCap;   // block-table entries per stream
   constexpr int CPR = D / 8;                  // 16-byte chunks per bf16 row
-  constexpr int SLOTS = KBK * CPR;
+  constexpr int SLOTS = V8 ? KBK * D / 16 : KBK * CPR;   // 16-byte slots of a V block
   constexpr int LPT = SLOTS / TS;             // V DMA loads per thread per block
   constexpr int KCPR = K8 ? D / 16 : CPR;     // 16-byte chunks per K row
   constexpr int LPK = KBK * KCPR / TS;        // K DMA loads per thread per block
@@ -634,11 +651,16 @@ __device__ __forceinline__ void pingpong_attn(
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int slot = (wsi * LPT + i) * 64 + lane;
-    const int r = slot / CPR;
-    voff[i] = (uint32_t)((int64_t)r * L.sn * 2 + (((slot % CPR) ^ swz_v<CPR>(r)) << 4));
+    if constexpr (V8) {
+      voff[i] = (uint32_t)slot * 16u;           // a V block is one contiguous run of d x 64 bytes
+    } else {
+      const int r = slot / CPR;
+      voff[i] = (uint32_t)((int64_t)r * L.sn * 2 + (((slot % CPR) ^ swz_v<CPR>(r)) << 4));
+    }
   }
   const char* kbase = reinterpret_cast<const char*>(k + head_off);
-  const char* vbase = reinterpret_cast<const char*>(v + head_off);
+  const char* vbase = V8 ? static_cast<const char*>(v) + (int64_t)bh * vt_head_bytes
+                         : reinterpret_cast<const char*>(static_cast<const uint16_t*>(v) + head_off);
   // One 16-byte-per-lane HBM -> LDS load.  Issued from inline assembly so that the
   // compiler's wait-count pass does not see it: it would otherwise wait for every LDS
   // DMA in flight before each LDS operand read.  All waits for these loads are explicit
@@ -656,9 +678,10 @@ __device__ __forceinline__ void pingpong_attn(
     constexpr int NL = IS_V ? LPT : LPK;
     constexpr int CP = IS_V ? CPR : KCPR;
     constexpr int EB = IS_V ? 2 : (int)sizeof(KT);
-    const char* g = base + blk.start * L.sn * EB;
+    constexpr bool BLOCKED = IS_V && V8;        // FP8 V: the 64-token block of the first key
+    const char* g = BLOCKED ? base + (blk.start >> 6) * (int64_t)(D * 64) : base + blk.start * L.sn * EB;
     const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t)(reinterpret_cast<char*>(dst) + wsi * NL * 1024);
-    if (blk.n == KBK) {
+    if (BLOCKED || blk.n == KBK) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         uint32_t o = off[i];
@@ -697,6 +720,9 @@ __device__ __forceinline__ void pingpong_attn(
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  f32x16 osum;                                // V8: every entry of a lane is its row's sum of weights
+#pragma unroll
+  for (int e = 0; e < 16; ++e) osum[e] = 0.f;
   float m_run = -INFINITY;
   float l_run = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -720,12 +746,14 @@ __device__ __forceinline__ void pingpong_attn(
     // operand addresses: group base plus the lane's swizzled offset for every K column
     // step and every V column block; stage and row offsets are instruction immediates
     const uint32_t gbase = (uint32_t)(uintptr_t)(lds_void_t)Gb;
-    uint32_t kA[K8 ? 2 * (D / 64) : D / 16], vA[D / 32];
+    uint32_t kA[K8 ? 2 * (D / 64) : D / 16], vA[D / 32], vB[2];
     if constexpr (K8) {
       // FP8: product ks reads the 16-byte chunks 4 ks + 2 hi and 4 ks + 2 hi + 1 of row l32
+      // (V8: of the permuted row, 16 rows further for the second 32-row tile)
+      const int kr = V8 ? 32 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3) : l32;
 #pragma unroll
       for (int c = 0; c < 2 * (D / 64); ++c) {
-        kA[c] = gbase + (uint32_t)l32 * D + ((uint32_t)((4 * (c >> 1) + 2 * hi + (c & 1)) ^ kswz(l32)) << 4);
+        kA[c] = gbase + (uint32_t)kr * D + ((uint32_t)((4 * (c >> 1) + 2 * hi + (c & 1)) ^ kswz(kr)) << 4);
         asm volatile("" : "+v"(kA[c]));
       }
     } else {
@@ -739,6 +767,15 @@ __device__ __forceinline__ void pingpong_attn(
     for (int db = 0; db < D / 32; ++db) {
       vA[db] = gbase + (vR ^ (db << 6));
       asm volatile("" : "+v"(vA[db]));
+    }
+    if constexpr (V8) {
+      // V^T operand: row 32 db + l32 of the block (64 bytes), keys 32 hi .. 32 hi + 31, i.e.
+      // logical chunks 2 hi and 2 hi + 1, swizzled by (row >> 1) & 3 like the quantiser
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        vB[part] = gbase + (uint32_t)l32 * 64 + ((uint32_t)((2 * hi + part) ^ ((l32 >> 1) & 3)) << 4);
+        asm volatile("" : "+v"(vB[part]));
+      }
     }
     // A products slot with no previous block multiplies P = 0 by a V stage: both stages
     // start zeroed so that a stage no DMA has filled yet holds finite values.
@@ -788,6 +825,11 @@ __device__ __forceinline__ void pingpong_attn(
     for (int c = 0; c < PC; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)0.f;
+    // V8: P^T as the second product's B operand, byte 16 mb + e of a lane = weight of
+    // accumulator entry (mb, e) = key 32 hi + 16 mb + e
+    i32x8 pb8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    const i32x8 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                         0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3FN 1.0
 
     typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8_t;
     auto read_v = [&](int ST, bf16x8 (&va)[D / 32][PC]) {   // V stage ST
@@ -817,8 +859,8 @@ __device__ __forceinline__ void pingpong_attn(
       for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const i32x4 a = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks] + ST * KBK * D * 2 + mb * 32 * D);
-          const i32x4 b = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks + 1] + ST * KBK * D * 2 + mb * 32 * D);
+          const i32x4 a = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks] + ST * KBK * D * 2 + mb * (V8 ? 16 : 32) * D);
+          const i32x4 b = *(lds_i32x4_t)(uintptr_t)(kA[2 * ks + 1] + ST * KBK * D * 2 + mb * (V8 ? 16 : 32) * D);
           ka[mb][ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
@@ -860,10 +902,34 @@ __device__ __forceinline__ void pingpong_attn(
     auto mphase = [&](auto stage) {
       constexpr int ST = decltype(stage)::value;
       bf16x8 va[D / 32][PC];
-      read_v(1 - ST, va);
+      if constexpr (!V8) read_v(1 - ST, va);
       // V reads (2 per PV product), then K reads; 8 reads go first, then each PV
       // product is followed by two reads, the last four by one
-      if constexpr (K8) {
+      if constexpr (V8) {
+        // V^T operands (two 16-byte reads per 32-row block), K operands, then the products:
+        // PV of c_{j-1} per 32 rows of d, the row sums, S^T of c_j
+        i32x8 va8[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const i32x4 a = *(lds_i32x4_t)(uintptr_t)(vB[0] + (2 + (1 - ST)) * KBK * D * 2 + db * 32 * 64);
+          const i32x4 b = *(lds_i32x4_t)(uintptr_t)(vB[1] + (2 + (1 - ST)) * KBK * D * 2 + db * 32 * 64);
+          va8[db] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        i32x8 ka[2][D / 64];
+        read_k8(ST, ka);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va8[db], pb8, o[db], 0, 0, 0, 127, 0, 127);
+        osum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pb8, osum, 0, 0, 0, 127, 0, 127);
+        mul_s8(ka);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * NS / (D / 32), 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1 + NS, 0);
+      } else if constexpr (K8) {
         i32x8 ka[2][D / 64];
         read_k8(ST, ka);
         mul_pv(va);
@@ -934,14 +1000,15 @@ __device__ __forceinline__ void pingpong_attn(
       if (cur.n > 0) {
         const int n = cur.n;
         if (n < KBK) {
-          int kb = hi * 4;
+          int kb = V8 ? hi * 32 : hi * 4;
           float ninf = -INFINITY;
           asm volatile("" : "+v"(kb), "+v"(ninf) : : "memory");
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-              const int c = mb * 32 + (e >> 2) * 8 + (e & 3);
+              // key of accumulator entry (mb, e) is kb + c (V8: the permuted K rows)
+              const int c = V8 ? mb * 16 + e : mb * 32 + (e >> 2) * 8 + (e & 3);
               if (kb >= n - c) s[mb][e] = ninf;
             }
         }
@@ -964,6 +1031,41 @@ __device__ __forceinline__ void pingpong_attn(
           }
           return bs;
         };
+        if constexpr (V8) {
+          // Weights are kept against the running maximum while no exponent exceeds kW8Lazy;
+          // otherwise (the first block too) the maximum moves to this block's.  The row sum
+          // comes from the products slot (an all-ones MFMA over the FP8 weights).
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+          if (__builtin_amdgcn_ballot_w64(!(fmaf(mx, scale_log2, -m_run) <= kW8Lazy)) != 0) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) osum[e] *= alpha;
+          }
+          // dword w of the B operand: keys 4w..4w+3 of this lane's 32, E4M3FN nearest even
+          const float off = kW8Shift - m_run;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const int mb = w >> 2, e = 4 * (w & 3);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[mb][e + 0], scale_log2, off));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mb][e + 1], scale_log2, off));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(s[mb][e + 2], scale_log2, off));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(s[mb][e + 3], scale_log2, off));
+            int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+            pb8[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, dw, true);
+          }
+        } else {
         float bs = weights();
         // Weights are kept while no lane's weights (16 per 32 keys) sum above kLazySum
         // (none exceeds it then).  Otherwise (the first block: m_run = -inf gives inf or NaN)
@@ -987,12 +1089,15 @@ __device__ __forceinline__ void pingpong_attn(
           bs = weights();
         }
         l_run += bs;
+        }
       } else {
         // no block: the next PV adds zero
 #pragma unroll
         for (int c = 0; c < PC; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pb8[w] = 0;
       }
       const Block nx3{(int64_t)__builtin_amdgcn_readfirstlane(e3.x), __builtin_amdgcn_readfirstlane(e3.y)};
       xo = Block{(int64_t)__builtin_amdgcn_readfirstlane(eo.x), __builtin_amdgcn_readfirstlane(eo.y)};
@@ -1023,6 +1128,7 @@ __device__ __forceinline__ void pingpong_attn(
   else
     body(std::integral_constant<int, 1>{});
 
+  if constexpr (V8) l_run = osum[0];            // the whole row's sum, in both halves
   // ---- merge group 1's partial result into group 0's (K/V stages are free now).  Each
   // wave of group 1 parks its D/32 accumulator tiles (16 floats per lane each) in sg0:
   // (D/32) * 4 float4 per lane, so NW waves fill exactly sg0 at either head dimension.
@@ -1059,9 +1165,12 @@ __device__ __forceinline__ void pingpong_attn(
     m_run = m;
   }
 
-  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  float l_tot = l_run;
+  if constexpr (!V8) {
+    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+  }
+  const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;
   if (q_ok) {
     uint16_t* op = out + head_off + my_q * L.sn;
 #pragma unroll
@@ -1079,8 +1188,9 @@ __device__ __forceinline__ void pingpong_attn(
         *reinterpret_cast<uint2*>(op + d0) = w;
       }
     if (lse && hi == 0) {
+      const float m_lse = V8 ? m_run - kW8Shift : m_run;   // V8: the weights carry 2^kW8Shift
       lse[(int64_t)bh * L.qlen + (my_q - L.q0)] =
-          (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+          (m_lse + __log2f(l_tot)) * 0.69314718055994530942f;
     }
   }
 }
@@ -1112,6 +1222,18 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_fp8qk_pingpong_kernel(
     const float* __restrict__ q_scale, const float* __restrict__ k_scale, uint16_t* __restrict__ out,
     float* __restrict__ lse, int by_heads) {
   pingpong_attn<D, true, false>(L, DN, q, k, v, idx, scale_log2 * q_scale[0] * k_scale[0], out, lse, by_heads);
+}
+
+// Q and K as above, V as FP8 codes in d-major 64-token blocks, P rounded to E4M3FN: both
+// products on the f8f6f4 matrix cores; the output is v_scale * sum(p v) / sum(p).
+template <int D>
+__global__ __launch_bounds__(512, 1) void sparse_attn_fp8_pingpong_kernel(
+    LayerDev L, DenseDev DN, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ vt, int64_t vt_head_bytes, const int32_t* __restrict__ idx, float scale_log2,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, true, false, true>(L, DN, q, k, vt, idx, scale_log2 * q_scale[0] * k_scale[0], out, lse,
+                                      by_heads, vt_head_bytes, v_scale[0]);
 }
 
 }  // namespace
@@ -1192,6 +1314,28 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void*
   else
     hipLaunchKernelGGL((sparse_attn_kernel<64, 2, 32>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
                        scale_log2, oo, lse, by_heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& DN, const void* q8, const void* k8,
+                                  const void* vt, int64_t n_tokens, const int32_t* idx, float scale,
+                                  const float* q_scale, const float* k_scale, const float* v_scale, void* out,
+                                  float* lse, hipStream_t s) {
+  dim3 grid;
+  int by_heads;
+  if (!grid_of(L, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  const int64_t vt_head_bytes = (n_tokens + 63) / 64 * (int64_t)L.d * 64;
+  auto qq = static_cast<const uint8_t*>(q8);
+  auto kk = static_cast<const uint8_t*>(k8);
+  auto vv = static_cast<const uint8_t*>(vt);
+  auto oo = static_cast<uint16_t*>(out);
+  if (L.d == 128)
+    hipLaunchKernelGGL((sparse_attn_fp8_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv,
+                       vt_head_bytes, idx, scale_log2, q_scale, k_scale, v_scale, oo, lse, by_heads);
+  else
+    hipLaunchKernelGGL((sparse_attn_fp8_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv,
+                       vt_head_bytes, idx, scale_log2, q_scale, k_scale, v_scale, oo, lse, by_heads);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 4
+#define VEDA_ABI_VERSION 5
 #define VEDA_MAX_SEGMENTS 4
 #define VEDA_MAX_DENSE 8
 #define VEDA_MAX_KEY_TILES 8192   /* sum over segments of T_s accepted by selection */
@@ -252,6 +252,51 @@ int veda_sparse_attn_fp8qk(const veda_layer* layer, const uint8_t* q8, const uin
  */
 int veda_quantize_fp8_e4m3(const veda_layer* layer, const void* x, uint8_t* x8, float* scale,
                            void* stream);
+
+/*
+ * FP8 attention with both products on the FP8 matrix cores (row f4 of the scope: the
+ * VDN article "VDN-H3 Renders Video Faster Than It Plays", section "Where it falls
+ * down", names a dedicated FP8 path; the Veda R2VA record, first paragraph, and the
+ * OpenVDN/vdn-minimax-h3 card, "Download the weights", ship FP8 streams.  The pages do
+ * not say how P is held; here it is E4M3FN).
+ * q8, k8, q_scale, k_scale as in veda_sparse_attn_fp8qk; vt and v_scale as
+ * veda_quantize_fp8_e4m3_vt writes them (vt device, veda_fp8_vt_bytes bytes, 16-byte
+ * aligned).  Per (b, h, query row) with the logits s_m of veda_sparse_attn_fp8qk over
+ * the same key set:
+ *     w_m = e4m3(16 exp(s_m - M)),  out = v_scale * sum_m w_m v8_m / sum_m w_m
+ * where v8_m is the decoded code of V row m, M a running maximum of the row's logits
+ * (one of them, at most 4.5 ln 2 below the largest logit of the key block, so
+ * w_m < 2^8.5) and e4m3 rounds to nearest even; the normaliser sums exactly the rounded
+ * weights.  Scaled so that the row's largest exact weight exp(s_m - max s) is 1, each
+ * weight is off its exact value p_m by at most 2^-4 p_m where p_m >= 2^-10, and by at
+ * most min(p_m, 2^-14) below that (subnormal codes; weights under 2^-14 may round to 0),
+ * by a rounding that depends on the block order (callers cannot predict it).  lse_opt
+ * (if given) is log(sum_m w_m exp(M) / 16), the row's log-sum-exp over the rounded
+ * weights.
+ * Needs 128-row tiles, segment and dense-range starts on multiples of 64 tokens, at
+ * most 3072 64-key blocks per query tile (else VEDA_EUNSUPPORTED); strides of q8, k8 as
+ * for veda_sparse_attn_fp8qk.  Every other argument and status as in veda_sparse_attn.
+ */
+int veda_sparse_attn_fp8(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const uint8_t* vt,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
+                         void* out, float* lse_opt, void* stream);
+
+/*
+ * V for veda_sparse_attn_fp8: v bf16 [B, n_tokens, H, d] (layer strides, 16-byte
+ * aligned) -> vt, E4M3FN codes in d-major blocks of 64 tokens, [B, H, ceil(n_tokens /
+ * 64), d, 64] bytes with each 64-byte row's four 16-byte chunks permuted: row c of block
+ * g keeps the codes of tokens 64 g + 16 j .. 64 g + 16 j + 15 in chunk j ^ ((c >> 1) & 3).
+ * Tokens past n_tokens are code 0.  *v_scale and the codes as veda_quantize_fp8_e4m3
+ * (the same per-tensor power of two, the same rounding).  Four launches on `stream`.
+ */
+int veda_quantize_fp8_e4m3_vt(const veda_layer* layer, const void* v, uint8_t* vt, float* v_scale,
+                              void* stream);
+
+/* Bytes of veda_quantize_fp8_e4m3_vt's output for this layer: B * H * ceil(n_tokens / 64)
+ * * d * 64.  Returns 0 for an invalid layer, or when B * H * ceil(n_tokens / 64) exceeds
+ * 2^31 - 1 (the two FP8-V entry points then return VEDA_EUNSUPPORTED). */
+size_t veda_fp8_vt_bytes(const veda_layer* layer);
 
 /*
  * Host-only check of a veda_sparse_attn call: returns the status veda_sparse_attn

@@ -254,6 +254,22 @@ void fuzz_layer(Rng& r, const veda_layer& L, int64_t room) {
     check_status("veda_quantize_fp8_e4m3", st, c3);
     if (!bad && !stub::fail_launch) EXPECT(st == c0, "veda_quantize_fp8_e4m3", st);
 
+    // the FP8-V form: the fp8qk checks plus 64-aligned segment and dense starts
+    Call c8(L);
+    st = veda_sparse_attn_fp8(&L, static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
+                              static_cast<const uint8_t*>(v), qs, qs, r.chance(2) ? nullptr : qs, idx, dp, nd,
+                              scale, out, lse, nullptr);
+    check_status("veda_sparse_attn_fp8", st, c8);
+    if (chk != VEDA_OK) EXPECT(st == chk, "veda_sparse_attn_fp8", st);
+
+    Call c9(L);
+    st = veda_quantize_fp8_e4m3_vt(&L, v, static_cast<uint8_t*>(dev(18)), static_cast<float*>(dev(19)), nullptr);
+    check_status("veda_quantize_fp8_e4m3_vt", st, c9);
+    const size_t vt_bytes = veda_fp8_vt_bytes(&L);
+    if (c0 != VEDA_OK) EXPECT(vt_bytes == 0, "veda_fp8_vt_bytes", c0);
+    const int c9w = c0 == VEDA_OK && vt_bytes == 0 ? VEDA_EUNSUPPORTED : c0;
+    if (!bad && !stub::fail_launch) EXPECT(st == c9w, "veda_quantize_fp8_e4m3_vt", st);
+
     Call c4(L);
     float* mass = static_cast<float*>(dev(20));
     st = veda_block_mass(&L, q, k, dp, nd, scale, static_cast<float*>(dev(21)), mass,

@@ -150,6 +150,28 @@ hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& D, const 
   return done();
 }
 
+hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& D, const void* q8, const void* k8,
+                                  const void* vt, int64_t n_tokens, const int32_t* idx, float scale,
+                                  const float* q_scale, const float* k_scale, const float* v_scale, void* out,
+                                  float* lse, hipStream_t) {
+  check_attn(L, D, q8, k8, vt, idx, scale, out, lse, __func__);
+  REQUIRE(L.tile == 128 && stub::fits);
+  REQUIRE(n_tokens == stub::n_tokens);
+  REQUIRE(L.sb % 16 == 0 && L.sn % 16 == 0 && L.sh % 16 == 0);
+  REQUIRE(q_scale && k_scale && v_scale && aligned(q_scale, 4) && aligned(k_scale, 4) && aligned(v_scale, 4));
+  for (int s = 0; s < L.n_seg; ++s) REQUIRE(L.seg[s].start % 64 == 0);
+  for (int i = 0; i < D.n; ++i) REQUIRE(D.r[i].start % 64 == 0);
+  return done();
+}
+
+hipError_t launch_quantize_fp8_vt(const LayerDev& L, int64_t n_tokens, const void* v, uint8_t* vt,
+                                  float* scale, hipStream_t) {
+  check_layer(L, __func__, false);
+  REQUIRE(n_tokens == stub::n_tokens);
+  REQUIRE(v && vt && scale && aligned(v, 16) && aligned(vt, 16) && aligned(scale, 4));
+  return done();
+}
+
 bool two_group_fits(const LayerDev& L, const DenseDev&) {
   check_layer(L, __func__);
   return stub::fits;
