@@ -6,8 +6,8 @@
 // dot product <q_hat_i, k_hat_j> of the projected pooled vectors; ties go to
 // the lower tile index and the chosen ids are written ascending.
 //
-// One workgroup (16 waves for predictor widths up to 64, 8 up to 128, else 4) owns R
-// consecutive query-tile rows of one (b, h):
+// One workgroup (8 or 16 waves for predictor widths up to 64, as topk_plan picks; 8 up to
+// 128, else 4) owns R consecutive query-tile rows of one (b, h):
 //  1. S[R x Tk] on bf16 matrix cores: each fp32 operand x is split into
 //     hi = bf16(x) and lo = bf16(x - hi); S = hi*hi + hi*lo + lo*hi (the lo*lo
 //     term is below 2^-16 relative).  v_mfma_f32_16x16x32_bf16 blocks of 16 key
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * kWaves) void score_topk_kernel(LayerDev L, int
   const int row0 = blockIdx.x * R;
   const int nrows = min(R, L.Tq - row0);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int P = L.p;
   const int64_t bh = (int64_t)b * L.H + h;
@@ -285,62 +285,85 @@ __global__ __launch_bounds__(64 * kWaves) void score_topk_kernel(LayerDev L, int
   }
 }
 
-// Waves per workgroup and histogram copies per wave for a predictor width: 16 waves (so
-// that one workgroup works on 16 rows at once and hides the latency of each row's serial
-// radix steps) where the kernel's registers allow it, fewer for wide predictors.
+// Waves per workgroup and histogram copies per wave for a predictor width: more waves
+// (one row each in the top-k phase) hide the latency of each row's serial radix steps, as
+// far as the kernel's registers allow.
 template <int kMaxKSteps>
 struct TopkShape {
   static constexpr int waves = kMaxKSteps <= 2 ? 16 : kMaxKSteps <= 4 ? 8 : 4;
   static constexpr int copies = kMaxKSteps <= 2 ? 1 : 4;
 };
+// Predictor widths up to 64 also have an 8-wave form: two of its workgroups share a CU
+// (its registers allow 16 waves per CU, not the 32 two 16-wave workgroups would need), so
+// one workgroup's top-k phase runs beside the other's score phase.
+struct TopkHalf {
+  static constexpr int waves = 8;
+  static constexpr int copies = 1;
+};
 
 }  // namespace
 
-// LDS bytes of one workgroup's histograms for a predictor width p
-static int hist_bytes(int p) {
-  auto f = [](auto shape) { return shape.waves * hist_words(shape.copies) * 4; };
-  if (p <= 64) return f(TopkShape<2>{});
-  if (p <= 128) return f(TopkShape<4>{});
-  if (p <= 256) return f(TopkShape<8>{});
-  return f(TopkShape<12>{});
+// Launch plan of the selection kernel for Tk key tiles and predictor width p: the form
+// (waves, histogram copies) and the rows R of the score block per workgroup.  Two
+// workgroups share a CU when each needs at most 78 KB of LDS and holds at least 8 rows;
+// otherwise one workgroup takes up to 150 KB.  At most 16 rows (one MFMA row block).
+struct TopkPlan {
+  int waves, copies, rows;
+  size_t lds;
+};
+
+static TopkPlan topk_plan(int Tk, int p) {
+  auto rows = [&](int waves, int copies, int budget) {
+    return (budget - waves * hist_words(copies) * 4) / (Tk * 4);
+  };
+  auto make = [&](int waves, int copies, int r) {
+    r = r > 16 ? 16 : (r < 1 ? 1 : r);
+    return TopkPlan{waves, copies, r, (size_t)r * Tk * 4 + (size_t)waves * hist_words(copies) * 4};
+  };
+  if (p <= 64) {
+    const int r2 = rows(TopkHalf::waves, TopkHalf::copies, 78 * 1024);
+    if (r2 >= 8) return make(TopkHalf::waves, TopkHalf::copies, r2);
+    return make(TopkShape<2>::waves, TopkShape<2>::copies,
+                rows(TopkShape<2>::waves, TopkShape<2>::copies, 150 * 1024));
+  }
+  auto generic = [&](auto shape) {
+    using S = decltype(shape);
+    const int r2 = rows(S::waves, S::copies, 78 * 1024);
+    return make(S::waves, S::copies, r2 >= 8 ? r2 : rows(S::waves, S::copies, 150 * 1024));
+  };
+  if (p <= 128) return generic(TopkShape<4>{});
+  if (p <= 256) return generic(TopkShape<8>{});
+  return generic(TopkShape<12>{});
 }
 
-int score_rows_per_block(int Tk, int p) {
-  // Prefer a block that lets two workgroups share a CU (<= 78 KB of LDS each); fall
-  // back to one workgroup per CU with up to 150 KB when fewer than 8 rows would fit.
-  const int hist = hist_bytes(p);
-  int r = (78 * 1024 - hist) / (Tk * 4);
-  if (r < 8) r = (150 * 1024 - hist) / (Tk * 4);
-  if (r > 16) r = 16;
-  if (r < 1) r = 1;
-  return r;
-}
+int score_rows_per_block(int Tk, int p) { return topk_plan(Tk, p).rows; }
 
 hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float* k_hat,
                              int32_t* idx, float* scores, hipStream_t s) {
-  const int R = score_rows_per_block(L.Tk, L.p);
-  const size_t lds = (size_t)R * L.Tk * 4 + hist_bytes(L.p);
+  const TopkPlan plan = topk_plan(L.Tk, L.p);
+  const int R = plan.rows;
   dim3 grid((unsigned)((L.Tq + R - 1) / R), (unsigned)L.H, (unsigned)L.B);
   // the kernel is instantiated for 32-wide predictor steps: p <= 64, 128, 256, 384
-  auto run = [&](auto kern, int waves) -> hipError_t {
-    if (lds > 64 * 1024) {
+  auto run = [&](auto kern) -> hipError_t {
+    if (plan.lds > 64 * 1024) {
       hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, s, L, R, q_hat, k_hat, idx, scores);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * plan.waves), plan.lds, s, L, R, q_hat, k_hat, idx, scores);
     return hipSuccess;
   };
-  auto go = [&](auto shape, auto kern) { return run(kern, decltype(shape)::waves); };
   hipError_t e;
-  if (L.p <= 64)
-    e = go(TopkShape<2>{}, score_topk_kernel<2, TopkShape<2>::waves, TopkShape<2>::copies>);
+  if (L.p <= 64 && plan.waves == TopkHalf::waves)
+    e = run(score_topk_kernel<2, TopkHalf::waves, TopkHalf::copies>);
+  else if (L.p <= 64)
+    e = run(score_topk_kernel<2, TopkShape<2>::waves, TopkShape<2>::copies>);
   else if (L.p <= 128)
-    e = go(TopkShape<4>{}, score_topk_kernel<4, TopkShape<4>::waves, TopkShape<4>::copies>);
+    e = run(score_topk_kernel<4, TopkShape<4>::waves, TopkShape<4>::copies>);
   else if (L.p <= 256)
-    e = go(TopkShape<8>{}, score_topk_kernel<8, TopkShape<8>::waves, TopkShape<8>::copies>);
+    e = run(score_topk_kernel<8, TopkShape<8>::waves, TopkShape<8>::copies>);
   else
-    e = go(TopkShape<12>{}, score_topk_kernel<12, TopkShape<12>::waves, TopkShape<12>::copies>);
+    e = run(score_topk_kernel<12, TopkShape<12>::waves, TopkShape<12>::copies>);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
