@@ -971,6 +971,18 @@ __device__ __forceinline__ void pingpong_attn(
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
+      if constexpr (K8) {
+        // The FP8 products have no side effects and nothing in this block reads their
+        // results, so the compiler would move them past the DMA's branch below, behind
+        // a DMA issue that can stall for hundreds of cycles.  An empty use keeps them here.
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(s[mb]));
+        if constexpr (V8) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(o[db]));
+          asm volatile("" : "+v"(osum));
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       int nc = 0;
       if (xo.n > 0) {
