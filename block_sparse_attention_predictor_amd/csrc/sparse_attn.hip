@@ -1047,11 +1047,13 @@ __device__ __forceinline__ void pingpong_attn(
           // Weights are kept against the running maximum while no exponent exceeds kW8Lazy;
           // otherwise (the first block too) the maximum moves to this block's.  The row sum
           // comes from the products slot (an all-ones MFMA over the FP8 weights).
-          float mx = -INFINITY;
+          // four independent max chains (a single chain of 16 dependent max3 waits on each)
+          float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+            for (int e = 0; e < 16; ++e) mq[e & 3] = fmaxf(mq[e & 3], s[mb][e]);
+          float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
           if (__builtin_amdgcn_ballot_w64(!(fmaf(mx, scale_log2, -m_run) <= kW8Lazy)) != 0) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
@@ -1074,7 +1076,9 @@ __device__ __forceinline__ void pingpong_attn(
             const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mb][e + 1], scale_log2, off));
             const float p2 = __builtin_amdgcn_exp2f(fmaf(s[mb][e + 2], scale_log2, off));
             const float p3 = __builtin_amdgcn_exp2f(fmaf(s[mb][e + 3], scale_log2, off));
-            int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+            // the first conversion writes bytes 0-1 and the second bytes 2-3, so the old
+            // value passed to the first (the previous block's dword) is fully replaced
+            const int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb8[w], false);
             pb8[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, dw, true);
           }
         } else {
