@@ -324,3 +324,39 @@ def test_fp8_entry_points_reject_before_device_calls():
     assert lib.veda_quantize_fp8_e4m3(ctypes.byref(L), fake, ctypes.c_void_p(0x10008), fake, None) == -1
     assert lib.veda_quantize_fp8_e4m3(ctypes.byref(L), fake, fake, ctypes.c_void_p(0x10001), None) == -1
     assert lib.veda_quantize_fp8_e4m3(ctypes.byref(_layer(d=96)), fake, fake, fake, None) == -2
+
+
+def test_fp8_v_entry_points_reject_before_device_calls():
+    """veda_sparse_attn_fp8 / veda_quantize_fp8_e4m3_vt / veda_fp8_vt_bytes: the blocked V size, and
+    every rejection the host makes before a launch (scales, strides, tile size, starts off a
+    multiple of 64 tokens, sizes the blocked layout cannot index)."""
+    lib = Bnd._load()
+    L = _layer()
+    n_blocks = -(-L.n_tokens // 64)
+    assert lib.veda_fp8_vt_bytes(ctypes.byref(L)) == L.B * L.H * n_blocks * L.d * 64
+    assert lib.veda_fp8_vt_bytes(ctypes.byref(_layer(d=96))) == 0
+    assert lib.veda_fp8_vt_bytes(None) == 0
+    fake = ctypes.c_void_p(0x10000)
+    dense, nd = Bnd.dense_ranges([(133056, 512), (133568, 256), (133824, 1024)])
+
+    def call(layer, qs=fake, ks=fake, vs=fake, dn=dense, n=nd):
+        return lib.veda_sparse_attn_fp8(ctypes.byref(layer), fake, fake, fake, qs, ks, vs, fake, dn, n, 0.0, fake,
+                                        None, None)
+    # missing or misaligned scales
+    assert call(L, vs=None) == -1
+    assert call(L, ks=ctypes.c_void_p(0x10002)) == -1
+    # dense ranges and segments must start on a multiple of 64 tokens (the blocked V layout)
+    off, no = Bnd.dense_ranges([(133056 + 32, 480), (133568, 256), (133824, 1024)])
+    assert call(L, dn=off, n=no) == -2
+    Ls = _layer()
+    Ls.seg[1].start += 32
+    Ls.seg[1].len -= 32
+    assert call(Ls) == -2
+    # 64-row tiles are not supported
+    assert call(_layer(tile=64)) == -2
+    # quantiser: null pointers, misaligned V, codes or scale
+    assert lib.veda_quantize_fp8_e4m3_vt(ctypes.byref(L), None, fake, fake, None) == -1
+    assert lib.veda_quantize_fp8_e4m3_vt(ctypes.byref(L), ctypes.c_void_p(0x10008), fake, fake, None) == -1
+    assert lib.veda_quantize_fp8_e4m3_vt(ctypes.byref(L), fake, ctypes.c_void_p(0x10008), fake, None) == -1
+    assert lib.veda_quantize_fp8_e4m3_vt(ctypes.byref(L), fake, fake, ctypes.c_void_p(0x10001), None) == -1
+    assert lib.veda_quantize_fp8_e4m3_vt(ctypes.byref(_layer(d=96)), fake, fake, fake, None) == -2
