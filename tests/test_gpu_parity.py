@@ -204,6 +204,50 @@ def test_topk_exact_ties_and_signed_zero():
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("K", [1, 7, 137, 256, 257, 2100])
+@pytest.mark.parametrize("kind", ["ties", "wide", "equal", "negative"])
+def test_topk_long_rows_exact(kind, K):
+    """Rows of 2100 key tiles (the length at which the top-k starts its radix below the top
+    bit, from the smallest of its group maxima and the largest key), with exact integer
+    scores: few values with many ties and signed zeros, values spread over many binades,
+    one value everywhere, all negative; budgets on both sides of 256 (the largest budget
+    that takes the bound) and the whole segment.  Bit-exact against the lowest-index rule;
+    a short second segment checks the rows that do not take the bound."""
+    g = np.random.default_rng(31 + K)
+    B, H, p, tile = 1, 2, 32, 64
+    Tq, T0, T1 = 6, 2100, 40
+    segs = [(0, T0 * tile, K), (T0 * tile, T1 * tile, 7)]
+    L = Bnd.make_layer(B=B, H=H, d=64, p=p, tile=tile, n_tokens=(T0 + T1) * tile,
+                       query=(0, Tq * tile), segments=segs, strides=((T0 + T1) * tile * H * 64, H * 64, 64))
+    qh = np.zeros((B, H, Tq, p), np.float32)
+    kh = np.zeros((B, H, T0 + T1, p), np.float32)
+    if kind == "ties":
+        qh[..., 0] = g.integers(-2, 3, (B, H, Tq))
+        qh[0, 0, 0, 0] = 1.0
+        kh[..., 0] = g.integers(-3, 4, (B, H, T0 + T1))
+        kh[0, 0, 5, 0] = -0.0
+    elif kind == "wide":      # integers up to 256 are exact in bf16, sums exact in fp32
+        qh[..., :2] = g.integers(-100, 101, (B, H, Tq, 2))
+        kh[..., :2] = g.integers(-200, 201, (B, H, T0 + T1, 2))
+    elif kind == "equal":
+        qh[..., 0] = 3.0
+        kh[..., 0] = 5.0
+    else:
+        qh[..., 0] = 1.0
+        kh[..., 0] = -g.integers(1, 201, (B, H, T0 + T1))
+    idx, sc = Bnd.score_topk(L, to_dev(qh), to_dev(kh), want_scores=True)
+    torch.cuda.synchronize()
+    S = qh.astype(np.float64) @ np.swapaxes(kh.astype(np.float64), -1, -2)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), S)
+    K0 = min(K, T0)
+    ref = np.zeros((B, H, Tq, K0 + 7), np.int32)
+    for h in range(H):
+        for i in range(Tq):
+            ref[0, h, i, :K0] = O.topk_lowest_index(S[0, h, i, :T0], K0)
+            ref[0, h, i, K0:] = O.topk_lowest_index(S[0, h, i, T0:], 7)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 # ----------------------------------------------------------------------------- a5
 
 def _oracle_attn_all(c, idx):
