@@ -17,7 +17,9 @@
 //    tile/32 waves, one pipeline (64-row tiles with 32-key blocks and four workgroups
 //    per CU);
 //  * sparse_attn_fp8qk_pingpong_kernel: the two-group kernel with Q and K as FP8
-//    (E4M3FN) codes and the first product on the FP8 matrix cores.
+//    (E4M3FN) codes and the first product on the FP8 matrix cores;
+//  * sparse_attn_fp8_pingpong_kernel: the same with V as FP8 too (d-major 64-token
+//    blocks) and P rounded to E4M3FN, both products on the FP8 matrix cores.
 //
 // Memory path (gfx950):
 //  * K and V rows go HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per
@@ -528,8 +530,8 @@ __device__ __forceinline__ int build_block_table(const LayerDev& L, const DenseD
 // bf16.  A K row is then d bytes: the K stages use the first half of their space, a
 // block's K DMA is half as many loads, and S^T takes 2 * d / 64 products instead of d / 8.
 //
-// V8 (with K8): V is FP8 too, in d-major blocks of 64 tokens (one 8 KB DMA per block,
-// see the V quantiser), and P is rounded to E4M3FN for the second product, also on the
+// V8 (with K8): V is FP8 too, in d-major blocks of 64 tokens (one contiguous DMA of d x 64
+// bytes per block, see the V quantiser), and P is rounded to E4M3FN for the second product, also on the
 // f8f6f4 matrix cores: O^T += V^T . P^T, A = V^T rows straight from LDS, B = P^T packed
 // from S^T's accumulators.  For that, S^T's K operand rows are read in a permuted order:
 // accumulator row 8 g + 4 h + t of the 32-row tile mb holds key 32 h + 16 mb + 4 g + t, so
