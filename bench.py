@@ -132,16 +132,21 @@ class Layer:
         self.L = B.layer_from_workload(wl)
         self.dense = [(r.start, r.length) for r in wl.dense]
         self.idx = torch.empty((wl.B, wl.H, wl.n_query_tiles, wl.k_total), dtype=torch.int32, device=dev)
+        self.order = torch.empty((wl.B, wl.H, wl.n_query_tiles), dtype=torch.int32, device=dev)
         self.ws = torch.empty(B.select_workspace_bytes(self.L) + 256, dtype=torch.uint8, device=dev)
         self.out = torch.zeros_like(self.qd)
         torch.cuda.synchronize()
 
     def select(self):
+        """The selection and the processing order of its query tiles (veda_tile_order)."""
         self.B.select(self.L, self.qd, self.kd, self.wq, self.wk, workspace=self.ws, idx=self.idx)
+        self.B.tile_order(self.L, self.idx, out=self.order)
 
     def attn(self, idx=None, L=None):
+        """Attention over the selection in its processing order, or over other index sets
+        (natural order)."""
         self.B.sparse_attn(L or self.L, self.qd, self.kd, self.vd, self.idx if idx is None else idx,
-                           self.dense, out=self.out)
+                           self.dense, out=self.out, order=self.order if idx is None else None)
 
     def step(self):
         self.select()
@@ -350,6 +355,9 @@ def measure(name, steps, warmup, kernel_reps, dense_reps, with_dense, log):
     _, _, pool_med = time_events(lambda: lay.B.project(lay.L, lay.qd, lay.kd, lay.wq, lay.wk), kernel_reps)
     res["pool_ms"] = pool_med
     res["pool_gbs"] = pool_bytes / (pool_med * 1e-3) / 1e9
+    # the processing-order kernel alone (part of selector_ms), median of kernel_reps
+    _, _, order_med = time_events(lambda: lay.B.tile_order(lay.L, lay.idx, out=lay.order), kernel_reps)
+    res["order_ms"] = order_med
     res["index_stats"] = index_stats(wl, idx_np)
     if with_dense:
         Lf, wlf = lay.full_budget_layer()
@@ -480,10 +488,10 @@ def measure_fp8(lay, kernel_reps, log):
         B.quantize_fp8_vt(lay.L, lay.vd, out=vt, scale=vs)
 
     def attn8():
-        B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, lay.idx, lay.dense, out=out8)
+        B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, lay.idx, lay.dense, out=out8, order=lay.order)
 
     def attn8v():
-        B.sparse_attn_fp8(lay.L, q8, k8, vt, qs, ks, vs, lay.idx, lay.dense, out=out8v)
+        B.sparse_attn_fp8(lay.L, q8, k8, vt, qs, ks, vs, lay.idx, lay.dense, out=out8v, order=lay.order)
 
     lay.select()
     lay.attn()
@@ -521,10 +529,10 @@ def measure_fp8(lay, kernel_reps, log):
             "kernel": f"sparse_attn_fp8_pingpong_kernel<{wl.d}>"}
     del out8, out8v
 
-    def attn8_with(idx):
+    def attn8_with(idx, order=None):
         """Both FP8 paths of this layer with the given index sets (for the parity leg)."""
-        return {"fp8qk": B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, idx, lay.dense),
-                "fp8": B.sparse_attn_fp8(lay.L, q8, k8, vt, qs, ks, vs, idx, lay.dense)}
+        return {"fp8qk": B.sparse_attn_fp8qk(lay.L, q8, k8, lay.vd, qs, ks, idx, lay.dense, order=order),
+                "fp8": B.sparse_attn_fp8(lay.L, q8, k8, vt, qs, ks, vs, idx, lay.dense, order=order)}
 
     return res, resv, attn8_with
 
@@ -633,10 +641,12 @@ def cpu_baseline(lay, log, budget_s=20.0, attn8_with=None):
             rows_outside += out_
     del sc_gpu
     # GPU attention fed the oracle's index sets (and the FP8 Q.K^T path, if given, likewise)
+    # (in their processing order, as the timed step runs)
     idx_ref_dev = torch.from_numpy(idx_ref).to(lay.qd.device)
-    out_gpu = lay.B.sparse_attn(lay.L, lay.qd, lay.kd, lay.vd, idx_ref_dev, lay.dense)
-    out8 = attn8_with(idx_ref_dev) if attn8_with is not None else {}
-    del idx_ref_dev
+    order_ref = lay.B.tile_order(lay.L, idx_ref_dev)
+    out_gpu = lay.B.sparse_attn(lay.L, lay.qd, lay.kd, lay.vd, idx_ref_dev, lay.dense, order=order_ref)
+    out8 = attn8_with(idx_ref_dev, order_ref) if attn8_with is not None else {}
+    del idx_ref_dev, order_ref
     torch.cuda.synchronize()
     # oracle attention on random (head, tile) pairs until the budget is used
     rng = np.random.default_rng(0)
@@ -811,6 +821,7 @@ def main():
                    "budgets": {s.name: s.budget for s in wl.segments},
                    "dense_tokens": sum(r.length for r in wl.dense), "seed": wl.index},
         "selector_ms": round(res["selector_ms"], 4),
+        "order_ms": round(res["order_ms"], 4),
         "full_layer_ms": round(res["full_layer_ms"], 4),
         "attn_ms": round(res["attn_ms"], 4),
         "dense_equiv_tflops_attn": round(res["dense_equiv_tflops_attn"], 2),

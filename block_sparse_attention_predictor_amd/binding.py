@@ -87,17 +87,18 @@ def _load():
         "veda_score_topk": (ctypes.c_int, [L, P, P, P, P, P]),
         "veda_select": (ctypes.c_int, [L, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "veda_select_noalloc": (ctypes.c_int, [L, P, P, P, P, P, P, P]),
-        "veda_sparse_attn": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+        "veda_sparse_attn": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                             ctypes.c_float, P, P, P]),
         "veda_dequant_fp8_e4m3": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
-        "veda_sparse_attn_fp8qk": (ctypes.c_int, [L, P, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+        "veda_sparse_attn_fp8qk": (ctypes.c_int, [L, P, P, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                                   ctypes.c_float, P, P, P]),
         "veda_quantize_fp8_e4m3": (ctypes.c_int, [L, P, P, P, P]),
-        "veda_sparse_attn_fp8": (ctypes.c_int, [L, P, P, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+        "veda_sparse_attn_fp8": (ctypes.c_int, [L, P, P, P, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                                 ctypes.c_float, P, P, P]),
         "veda_quantize_fp8_e4m3_vt": (ctypes.c_int, [L, P, P, P, P]),
         "veda_fp8_vt_bytes": (ctypes.c_size_t, [L]),
-        "veda_sparse_attn_check": (ctypes.c_int, [L, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
+        "veda_tile_order": (ctypes.c_int, [L, P, P, P]),
+        "veda_sparse_attn_check": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                                   ctypes.c_float, P]),
         "veda_layer_attn": (ctypes.c_int, [L, P, P, P, P, P, ctypes.POINTER(Range), ctypes.c_int32,
                                            ctypes.POINTER(Range), ctypes.c_int32, ctypes.c_float, P, P, P,
@@ -139,11 +140,11 @@ def exported_symbols():
                         "veda_st_find", "veda_st_read", "veda_st_metadata_count",
                         "veda_st_metadata_at", "veda_sparse_attn_fp8qk",
                         "veda_quantize_fp8_e4m3", "veda_sparse_attn_fp8", "veda_quantize_fp8_e4m3_vt",
-                        "veda_fp8_vt_bytes")]
+                        "veda_fp8_vt_bytes", "veda_tile_order")]
 
 
 # VEDA_ABI_VERSION of include/veda.h that this binding marshals for
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 def abi_version() -> int:
@@ -329,9 +330,34 @@ def select_noalloc(layer: Layer, q, k, wq, wk, idx, scores=None, stream=None):
     return idx
 
 
+def _check_order(layer: Layer, order, idx, device):
+    if order is None:
+        return
+    if idx is None:
+        raise ValueError("an order needs an index")
+    if order.dtype != torch.int32 or not order.is_contiguous() or \
+            tuple(order.shape) != (layer.B, layer.H, layer.Tq) or order.device != device:
+        raise ValueError(f"order must be a contiguous int32 [B, H, Tq] = {[layer.B, layer.H, layer.Tq]} "
+                         f"tensor on {device}")
+
+
+def tile_order(layer: Layer, idx, out=None, stream=None):
+    """veda_tile_order: int32 [B, H, Tq], per (b, h) the query tiles sorted by their index rows
+    (the processing order for the attention calls' `order` argument)."""
+    _check_idx(layer, idx, idx.device)
+    if out is None:
+        out = torch.empty((layer.B, layer.H, layer.Tq), dtype=torch.int32, device=idx.device)
+    _check_order(layer, out, idx, idx.device)
+    st = _load().veda_tile_order(ctypes.byref(layer), _ptr(idx), _ptr(out), _stream(stream))
+    _check(st, "veda_tile_order")
+    return out
+
+
 def sparse_attn(layer: Layer, q, k, v, idx, dense: Sequence[Tuple[int, int]] = (),
-                scale: float = 0.0, out=None, want_lse: bool = False, stream=None):
-    """Block-sparse attention; returns out (bf16, q's shape) [and lse fp32 [B, H, query.len]]."""
+                scale: float = 0.0, out=None, want_lse: bool = False, stream=None, order=None):
+    """Block-sparse attention; returns out (bf16, q's shape) [and lse fp32 [B, H, query.len]].
+    order: None, or tile_order's output (the query tiles' processing order; results do not
+    depend on it)."""
     _check_qkv(layer, q, k, v)
     if out is None:
         out = torch.zeros_like(q)
@@ -341,8 +367,9 @@ def sparse_attn(layer: Layer, q, k, v, idx, dense: Sequence[Tuple[int, int]] = (
         if want_lse else None
     if idx is not None:
         _check_idx(layer, idx, q.device)
+    _check_order(layer, order, idx, q.device)
     arr, n = dense_ranges(list(dense))
-    st = _load().veda_sparse_attn(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), arr, n,
+    st = _load().veda_sparse_attn(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(order), arr, n,
                                   float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "veda_sparse_attn")
     return (out, lse) if want_lse else out
@@ -379,7 +406,7 @@ def quantize_fp8(layer: Layer, x, out=None, scale=None, stream=None):
 
 
 def sparse_attn_fp8qk(layer: Layer, q8, k8, v, q_scale, k_scale, idx, dense: Sequence[Tuple[int, int]] = (),
-                      scale: float = 0.0, out=None, want_lse: bool = False, stream=None):
+                      scale: float = 0.0, out=None, want_lse: bool = False, stream=None, order=None):
     """veda_sparse_attn with E4M3FN Q and K (codes and per-tensor scales as quantize_fp8 returns
     them); v bf16.  Returns out (bf16, v's shape) [and lse fp32 [B, H, query.len]]."""
     _check_fp8(layer, q8, k8)
@@ -393,9 +420,10 @@ def sparse_attn_fp8qk(layer: Layer, q8, k8, v, q_scale, k_scale, idx, dense: Seq
         if want_lse else None
     if idx is not None:
         _check_idx(layer, idx, v.device)
+    _check_order(layer, order, idx, v.device)
     arr, n = dense_ranges(list(dense))
     st = _load().veda_sparse_attn_fp8qk(ctypes.byref(layer), _ptr(q8), _ptr(k8), _ptr(v), _ptr(q_scale),
-                                        _ptr(k_scale), _ptr(idx), arr, n, float(scale), _ptr(out), _ptr(lse),
+                                        _ptr(k_scale), _ptr(idx), _ptr(order), arr, n, float(scale), _ptr(out), _ptr(lse),
                                         _stream(stream))
     _check(st, "veda_sparse_attn_fp8qk")
     return (out, lse) if want_lse else out
@@ -432,7 +460,7 @@ def quantize_fp8_vt(layer: Layer, v, out=None, scale=None, stream=None):
 
 def sparse_attn_fp8(layer: Layer, q8, k8, vt, q_scale, k_scale, v_scale, idx,
                     dense: Sequence[Tuple[int, int]] = (), scale: float = 0.0, out=None, want_lse: bool = False,
-                    stream=None):
+                    stream=None, order=None):
     """veda_sparse_attn with E4M3FN Q, K (as quantize_fp8 returns them), V in the blocked layout
     of quantize_fp8_vt, and P rounded to E4M3FN.  Returns out (bf16, q8's shape and strides)
     [and lse fp32 [B, H, query.len]]."""
@@ -448,9 +476,10 @@ def sparse_attn_fp8(layer: Layer, q8, k8, vt, q_scale, k_scale, v_scale, idx,
         if want_lse else None
     if idx is not None:
         _check_idx(layer, idx, q8.device)
+    _check_order(layer, order, idx, q8.device)
     arr, n = dense_ranges(list(dense))
     st = _load().veda_sparse_attn_fp8(ctypes.byref(layer), _ptr(q8), _ptr(k8), _ptr(vt), _ptr(q_scale),
-                                      _ptr(k_scale), _ptr(v_scale), _ptr(idx), arr, n, float(scale), _ptr(out),
+                                      _ptr(k_scale), _ptr(v_scale), _ptr(idx), _ptr(order), arr, n, float(scale), _ptr(out),
                                       _ptr(lse), _stream(stream))
     _check(st, "veda_sparse_attn_fp8")
     return (out, lse) if want_lse else out

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libveda.so")
 SOURCES = ["api.cpp", "dequant.hip", "pool_project.hip", "score_topk.hip", "sparse_attn.hip",
-           "patterns.hip", "block_mass.hip", "safetensors.cpp", "noalloc.hip"]
+           "patterns.hip", "block_mass.hip", "safetensors.cpp", "noalloc.hip", "work_order.hip"]
 # measurement aids for benchmarks (include/veda_probe.h), a library of their own
 PROBE_SOURCES = ["probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libveda_probe.so")

@@ -202,12 +202,13 @@ namespace {
 
 // Every check veda_sparse_attn makes before launching; dd receives the dense ranges.
 int sparse_attn_check(const veda_layer* layer, const void* q, const void* k, const void* v,
-                      const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
-                      const void* out, veda::DenseDev* dd) {
+                      const int32_t* idx, const int32_t* order, const veda_range* dense, int32_t n_dense,
+                      float scale, const void* out, veda::DenseDev* dd) {
   int st = check_layer(layer, false);
   if (st != VEDA_OK) return st;
   if (!q || !k || !v || !out) return VEDA_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VEDA_EINVAL;
+  if (order && (!idx || (reinterpret_cast<uintptr_t>(order) & 3u))) return VEDA_EINVAL;
   if (n_dense < 0) return VEDA_EINVAL;
   if (n_dense > VEDA_MAX_DENSE) return VEDA_EUNSUPPORTED;
   if (n_dense > 0 && !dense) return VEDA_EINVAL;
@@ -244,31 +245,41 @@ int sparse_attn_check(const veda_layer* layer, const void* q, const void* k, con
 extern "C" {
 
 int veda_sparse_attn_check(const veda_layer* layer, const void* q, const void* k, const void* v,
-                           const int32_t* idx, const veda_range* dense, int32_t n_dense,
-                           float scale, const void* out) {
-  return sparse_attn_check(layer, q, k, v, idx, dense, n_dense, scale, out, nullptr);
+                           const int32_t* idx, const int32_t* order, const veda_range* dense,
+                           int32_t n_dense, float scale, const void* out) {
+  return sparse_attn_check(layer, q, k, v, idx, order, dense, n_dense, scale, out, nullptr);
+}
+
+int veda_tile_order(const veda_layer* layer, const int32_t* idx, int32_t* order, void* stream) {
+  int st = check_layer(layer, false);
+  if (st != VEDA_OK) return st;
+  if (!idx || !order) return VEDA_EINVAL;
+  if (!aligned16(idx) || (reinterpret_cast<uintptr_t>(order) & 3u)) return VEDA_EINVAL;
+  LayerDev D = to_dev(layer);
+  if (D.Tq == 0) return VEDA_OK;
+  return hip_status(veda::launch_tile_order(D, idx, order, (hipStream_t)stream));
 }
 
 int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
-                     const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
-                     void* out, float* lse_opt, void* stream) {
+                     const int32_t* idx, const int32_t* order, const veda_range* dense, int32_t n_dense,
+                     float scale, void* out, float* lse_opt, void* stream) {
   veda::DenseDev DD{};
-  int st = sparse_attn_check(layer, q, k, v, idx, dense, n_dense, scale, out, &DD);
+  int st = sparse_attn_check(layer, q, k, v, idx, order, dense, n_dense, scale, out, &DD);
   if (st != VEDA_OK) return st;
   if (lse_opt && !aligned16(lse_opt)) return VEDA_EINVAL;
   LayerDev D = to_dev(layer);
   if (D.Tq == 0) return VEDA_OK;
   if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
-  return hip_status(veda::launch_sparse_attn(D, DD, q, k, v, idx, scale, out, lse_opt,
+  return hip_status(veda::launch_sparse_attn(D, DD, q, k, v, idx, order, scale, out, lse_opt,
                                              (hipStream_t)stream));
 }
 
 int veda_sparse_attn_fp8qk(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const void* v,
                            const float* q_scale, const float* k_scale, const int32_t* idx,
-                           const veda_range* dense, int32_t n_dense, float scale, void* out,
-                           float* lse_opt, void* stream) {
+                           const int32_t* order, const veda_range* dense, int32_t n_dense, float scale,
+                           void* out, float* lse_opt, void* stream) {
   veda::DenseDev DD{};
-  int st = sparse_attn_check(layer, q8, k8, v, idx, dense, n_dense, scale, out, &DD);
+  int st = sparse_attn_check(layer, q8, k8, v, idx, order, dense, n_dense, scale, out, &DD);
   if (st != VEDA_OK) return st;
   if (!q_scale || !k_scale) return VEDA_EINVAL;
   if ((reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
@@ -281,7 +292,7 @@ int veda_sparse_attn_fp8qk(const veda_layer* layer, const uint8_t* q8, const uin
   if (D.Tq == 0) return VEDA_OK;
   if (!veda::two_group_fits(D, DD)) return VEDA_EUNSUPPORTED;
   if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
-  return hip_status(veda::launch_sparse_attn_fp8qk(D, DD, q8, k8, v, idx, scale, q_scale, k_scale, out,
+  return hip_status(veda::launch_sparse_attn_fp8qk(D, DD, q8, k8, v, idx, order, scale, q_scale, k_scale, out,
                                                    lse_opt, (hipStream_t)stream));
 }
 
@@ -316,10 +327,10 @@ int veda_quantize_fp8_e4m3_vt(const veda_layer* layer, const void* v, uint8_t* v
 
 int veda_sparse_attn_fp8(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const uint8_t* vt,
                          const float* q_scale, const float* k_scale, const float* v_scale,
-                         const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
-                         void* out, float* lse_opt, void* stream) {
+                         const int32_t* idx, const int32_t* order, const veda_range* dense, int32_t n_dense,
+                         float scale, void* out, float* lse_opt, void* stream) {
   veda::DenseDev DD{};
-  int st = sparse_attn_check(layer, q8, k8, vt, idx, dense, n_dense, scale, out, &DD);
+  int st = sparse_attn_check(layer, q8, k8, vt, idx, order, dense, n_dense, scale, out, &DD);
   if (st != VEDA_OK) return st;
   if (!q_scale || !k_scale || !v_scale) return VEDA_EINVAL;
   if ((reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
@@ -338,7 +349,7 @@ int veda_sparse_attn_fp8(const veda_layer* layer, const uint8_t* q8, const uint8
   if (D.Tq == 0) return VEDA_OK;
   if (!veda::two_group_fits(D, DD)) return VEDA_EUNSUPPORTED;
   if (scale == 0.f) scale = 1.0f / std::sqrt((float)layer->d);
-  return hip_status(veda::launch_sparse_attn_fp8(D, DD, q8, k8, vt, layer->n_tokens, idx, scale, q_scale,
+  return hip_status(veda::launch_sparse_attn_fp8(D, DD, q8, k8, vt, layer->n_tokens, idx, order, scale, q_scale,
                                                  k_scale, v_scale, out, lse_opt, (hipStream_t)stream));
 }
 
@@ -366,16 +377,21 @@ int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const
   if (!q || !k || !wq || !wk || !idx || !ws) return VEDA_EINVAL;
   LayerDev D = to_dev(layer);
   if (ws_bytes < qhat_bytes(D) + khat_bytes(D)) return VEDA_EWORKSPACE;
-  st = veda_sparse_attn_check(layer, q, k, v, idx, dense, n_dense, scale, out);
+  st = veda_sparse_attn_check(layer, q, k, v, idx, nullptr, dense, n_dense, scale, out);
   if (st != VEDA_OK) return st;
   for (int i = 0; i < n_dense_queries; ++i) {
     full.query = dense_queries[i];
-    st = veda_sparse_attn_check(&full, q, k, v, nullptr, dense, n_dense, scale, out);
+    st = veda_sparse_attn_check(&full, q, k, v, nullptr, nullptr, dense, n_dense, scale, out);
     if (st != VEDA_OK) return st;
   }
   st = veda_select(layer, q, k, wq, wk, idx, nullptr, ws, ws_bytes, stream);
   if (st != VEDA_OK) return st;
-  st = veda_sparse_attn(layer, q, k, v, idx, dense, n_dense, scale, out, nullptr, stream);
+  // the processing order goes into the workspace, free once the selection has run (its
+  // q_hat part alone, B*H*Tq*p floats, is larger)
+  int32_t* const order = static_cast<int32_t*>(ws);
+  st = veda_tile_order(layer, idx, order, stream);
+  if (st != VEDA_OK) return st;
+  st = veda_sparse_attn(layer, q, k, v, idx, order, dense, n_dense, scale, out, nullptr, stream);
   if (st != VEDA_OK) return st;
   // dense query ranges that touch each other run as one launch (every row attends to the
   // same keys, so grouping rows into tiles across a boundary changes nothing)
@@ -394,7 +410,7 @@ int veda_layer_attn(const veda_layer* layer, const void* q, const void* k, const
   }
   for (int i = 0; i < n_runs; ++i) {
     full.query = merged[i];
-    st = veda_sparse_attn(&full, q, k, v, nullptr, dense, n_dense, scale, out, nullptr, stream);
+    st = veda_sparse_attn(&full, q, k, v, nullptr, nullptr, dense, n_dense, scale, out, nullptr, stream);
     if (st != VEDA_OK) return st;
   }
   return VEDA_OK;
@@ -458,7 +474,7 @@ int veda_block_mass(const veda_layer* layer, const void* q, const void* k, const
     full.budget[s] = (int32_t)std::min<int64_t>(ceil_div(std::max<int64_t>(full.seg[s].len, 0),
                                                          std::max(full.tile, 1)), INT32_MAX);
   veda::DenseDev DD{};
-  int st = sparse_attn_check(&full, q, k, k, nullptr, dense, n_dense, scale, mass, &DD);
+  int st = sparse_attn_check(&full, q, k, k, nullptr, nullptr, dense, n_dense, scale, mass, &DD);
   if (st != VEDA_OK) return st;
   if (!lse || !aligned16(lse)) return VEDA_EINVAL;
   if (dense_mass_opt && !aligned16(dense_mass_opt)) return VEDA_EINVAL;

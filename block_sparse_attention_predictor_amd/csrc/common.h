@@ -46,14 +46,17 @@ hipError_t launch_pool_project(const LayerDev& L, const void* q, const void* k, 
                                const void* wk, float* q_hat, float* k_hat, hipStream_t s);
 hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float* k_hat,
                              int32_t* idx, float* scores, hipStream_t s);
+// order: NULL, or int32 [B, H, Tq], the query tile each (b, h)'s processing position
+// takes (see work_order.hip); only read when idx is given.
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& D, const void* q, const void* k,
-                              const void* v, const int32_t* idx, float scale, void* out,
+                              const void* v, const int32_t* idx, const int32_t* order, float scale, void* out,
                               float* lse, hipStream_t s);
 // Q and K as E4M3FN codes (same element strides as the bf16 tensors, one byte each) with
 // per-tensor scales in device memory; V, O as in launch_sparse_attn.  Needs 128-row tiles
 // and a block list within the two-group kernel's table (two_group_fits).
 hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& D, const void* q8, const void* k8,
-                                    const void* v, const int32_t* idx, float scale, const float* q_scale,
+                                    const void* v, const int32_t* idx, const int32_t* order, float scale,
+                                    const float* q_scale,
                                     const float* k_scale, void* out, float* lse, hipStream_t s);
 bool two_group_fits(const LayerDev& L, const DenseDev& D);
 // bf16 tensor [B, n_tokens, H, d] (layer strides) -> E4M3FN codes at the same element
@@ -71,9 +74,15 @@ hipError_t launch_quantize_fp8_vt(const LayerDev& L, int64_t n_tokens, const voi
 // E4M3FN for the second product.  Needs 128-row tiles, block starts on multiples of 64 and
 // a block list within the two-group kernel's table.
 hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& D, const void* q8, const void* k8,
-                                  const void* vt, int64_t n_tokens, const int32_t* idx, float scale,
+                                  const void* vt, int64_t n_tokens, const int32_t* idx, const int32_t* order,
+                                  float scale,
                                   const float* q_scale, const float* k_scale, const float* v_scale, void* out,
                                   float* lse, hipStream_t s);
+
+// Processing order of the query tiles (see work_order.hip): order int32 [B, H, Tq].
+// Layers with more than kOrderCap query tiles get the identity order.
+constexpr int kOrderCap = 16384;
+hipError_t launch_tile_order(const LayerDev& L, const int32_t* idx, int32_t* order, hipStream_t s);
 
 // Teacher block attention mass (two launches: dense lse, then per-tile mass) and the
 // recall of an index set under it (see block_mass.hip).  L must carry full budgets.

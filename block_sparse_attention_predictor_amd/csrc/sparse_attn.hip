@@ -160,12 +160,20 @@ __device__ __forceinline__ bool work_item(const LayerDev& L, int n, int by_heads
 __device__ __forceinline__ bool work_item(const LayerDev& L, int by_heads, int& bh, int& qt) {
   return work_item(L, L.Tq, by_heads, bh, qt);
 }
+// Query tile at processing position pos of (b, h): pos itself, or the caller's order
+// entry for it; -1 for none (pos past the last tile, or an entry outside [0, Tq)).
+__device__ __forceinline__ int tile_at(const LayerDev& L, const int32_t* order, int bh, int pos) {
+  if (pos >= L.Tq) return -1;
+  if (order == nullptr) return pos;
+  const int t = order[(int64_t)bh * L.Tq + pos];
+  return t >= 0 && t < L.Tq ? t : -1;
+}
 
 template <int D, int NW, int KBK>
 __global__ __launch_bounds__(64 * NW, KBK == 32 ? 4 : 2) void sparse_attn_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
   constexpr int NT = 64 * NW;                 // threads
   constexpr int CPR = D / 8;                  // 16-byte chunks per key row
   constexpr int SLOTS = KBK * CPR;            // 16-byte slots per K (or V) block
@@ -189,6 +197,7 @@ __global__ __launch_bounds__(64 * NW, KBK == 32 ? 4 : 2) void sparse_attn_kernel
 
   int bh, qt;
   if (!work_item(L, by_heads, bh, qt)) return;     // padding workgroup (uniform exit)
+  if (!by_heads && (qt = tile_at(L, order, bh, qt)) < 0) return;   // no tile at this position
   const int h = bh % L.H;
   const int b = bh / L.H;
 
@@ -544,8 +553,9 @@ template <int D, bool K8, bool T2, bool V8 = false>
 __device__ __forceinline__ void pingpong_attn(
     const LayerDev& L, const DenseDev& DN, const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ q,
     const std::conditional_t<K8, uint8_t, uint16_t>* __restrict__ k, const void* __restrict__ v,
-    const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    int by_heads, int64_t vt_head_bytes = 0, float out_scale = 1.0f) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ order, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads, int64_t vt_head_bytes = 0,
+    float out_scale = 1.0f) {
   using KT = std::conditional_t<K8, uint8_t, uint16_t>;
   static_assert(!(K8 && T2), "the FP8 form runs 128-row tiles only");
   static_assert(!V8 || K8, "FP8 V needs FP8 Q and K");
@@ -581,14 +591,18 @@ __device__ __forceinline__ void pingpong_attn(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // T2: a work item is the pair of query tiles 2 it and 2 it + 1 (the second one absent
-  // for the last item of an odd tile count)
+  // A work item is processing position it (T2: the pair of positions 2 it and 2 it + 1, the
+  // second one absent for the last item of an odd tile count); its query tile is the
+  // position itself or the caller's order entry for it (no tile: nothing to do)
   int bh, it;
   if (!work_item(L, T2 ? (L.Tq + 1) >> 1 : L.Tq, by_heads, bh, it)) return;   // padding workgroup
   const int h = bh % L.H;
   const int b = bh / L.H;
-  const int qt = T2 ? 2 * it + half : it;
-  const bool tile_ok = qt < L.Tq;
+  auto tile_of = [&](int pos) { return by_heads ? (pos < L.Tq ? pos : -1) : tile_at(L, order, bh, pos); };
+  const int qt_at = tile_of(T2 ? 2 * it + half : it);
+  if (!T2 && qt_at < 0) return;                   // uniform over the workgroup
+  const bool tile_ok = qt_at >= 0;
+  const int qt = tile_ok ? qt_at : 0;
 
   const int64_t q_first = L.q0 + (int64_t)qt * L.tile;
   const int64_t q_end = L.q0 + L.qlen;
@@ -621,9 +635,9 @@ __device__ __forceinline__ void pingpong_attn(
   // wave s (s < number of streams) builds stream s's table; a stream without a tile has none
   if (tid < (T2 ? 128 : 64)) {
     const int st = tid >> 6;
-    const int qts = T2 ? 2 * it + st : it;
+    const int qts = tile_of(T2 ? 2 * it + st : it);
     int n = 0;
-    if (qts < L.Tq) {
+    if (qts >= 0) {
       const int32_t* const row = idx ? idx + ((int64_t)bh * L.Tq + qts) * L.Ktot : nullptr;
       n = build_block_table<KBK, CAP>(L, DN, row, lane, stab + st * CAP);
     }
@@ -1216,9 +1230,9 @@ __device__ __forceinline__ void pingpong_attn(
 template <int D>
 __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
-  pingpong_attn<D, false, false>(L, DN, q, k, v, idx, scale_log2, out, lse, by_heads);
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, false, false>(L, DN, q, k, v, idx, order, scale_log2, out, lse, by_heads);
 }
 
 // 64-row tiles: one workgroup takes two neighbouring query tiles, waves 0-1 and 2-3 of each
@@ -1226,9 +1240,9 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_kernel(
 template <int D>
 __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_pair_kernel(
     LayerDev L, DenseDev DN, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
-  pingpong_attn<D, false, true>(L, DN, q, k, v, idx, scale_log2, out, lse, by_heads);
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, false, true>(L, DN, q, k, v, idx, order, scale_log2, out, lse, by_heads);
 }
 
 // Q and K as FP8 codes with per-tensor scales (device floats): logits are
@@ -1236,10 +1250,11 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_pingpong_pair_kernel(
 template <int D>
 __global__ __launch_bounds__(512, 1) void sparse_attn_fp8qk_pingpong_kernel(
     LayerDev L, DenseDev DN, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, float scale_log2,
-    const float* __restrict__ q_scale, const float* __restrict__ k_scale, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int by_heads) {
-  pingpong_attn<D, true, false>(L, DN, q, k, v, idx, scale_log2 * q_scale[0] * k_scale[0], out, lse, by_heads);
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, const int32_t* __restrict__ order,
+    float scale_log2, const float* __restrict__ q_scale, const float* __restrict__ k_scale,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, true, false>(L, DN, q, k, v, idx, order, scale_log2 * q_scale[0] * k_scale[0], out, lse,
+                                by_heads);
 }
 
 // Q and K as above, V as FP8 codes in d-major 64-token blocks, P rounded to E4M3FN: both
@@ -1247,11 +1262,12 @@ __global__ __launch_bounds__(512, 1) void sparse_attn_fp8qk_pingpong_kernel(
 template <int D>
 __global__ __launch_bounds__(512, 1) void sparse_attn_fp8_pingpong_kernel(
     LayerDev L, DenseDev DN, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-    const uint8_t* __restrict__ vt, int64_t vt_head_bytes, const int32_t* __restrict__ idx, float scale_log2,
-    const float* __restrict__ q_scale, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int by_heads) {
-  pingpong_attn<D, true, false, true>(L, DN, q, k, vt, idx, scale_log2 * q_scale[0] * k_scale[0], out, lse,
-                                      by_heads, vt_head_bytes, v_scale[0]);
+    const uint8_t* __restrict__ vt, int64_t vt_head_bytes, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ order, float scale_log2, const float* __restrict__ q_scale,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int by_heads) {
+  pingpong_attn<D, true, false, true>(L, DN, q, k, vt, idx, order, scale_log2 * q_scale[0] * k_scale[0], out,
+                                      lse, by_heads, vt_head_bytes, v_scale[0]);
 }
 
 }  // namespace
@@ -1296,49 +1312,50 @@ bool pair_fits(const LayerDev& L, const DenseDev& DN) {
 }
 
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void* q, const void* k,
-                              const void* v, const int32_t* idx, float scale, void* out, float* lse,
-                              hipStream_t s) {
+                              const void* v, const int32_t* idx, const int32_t* order, float scale, void* out,
+                              float* lse, hipStream_t s) {
   const bool two_group = two_group_fits(L, DN);
   const bool pair = pair_fits(L, DN);
   dim3 grid;
   int by_heads;
   if (!grid_of(L, pair ? ((int64_t)L.Tq + 1) / 2 : L.Tq, idx, grid, by_heads)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
+  const int32_t* const ord = idx ? order : nullptr;
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(out);
   if (pair && L.d == 128)
     hipLaunchKernelGGL((sparse_attn_pingpong_pair_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   else if (pair)
     hipLaunchKernelGGL((sparse_attn_pingpong_pair_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   else if (two_group && L.d == 128)
     hipLaunchKernelGGL((sparse_attn_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   else if (two_group)
     hipLaunchKernelGGL((sparse_attn_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   else if (L.d == 128 && L.tile == 128)
     hipLaunchKernelGGL((sparse_attn_kernel<128, 4, 64>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   else if (L.d == 128 && L.tile == 64)
     hipLaunchKernelGGL((sparse_attn_kernel<128, 2, 32>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   else if (L.d == 64 && L.tile == 128)
     hipLaunchKernelGGL((sparse_attn_kernel<64, 4, 64>), grid, dim3(256), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   else
     hipLaunchKernelGGL((sparse_attn_kernel<64, 2, 32>), grid, dim3(128), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, oo, lse, by_heads);
+                       ord, scale_log2, oo, lse, by_heads);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& DN, const void* q8, const void* k8,
-                                  const void* vt, int64_t n_tokens, const int32_t* idx, float scale,
-                                  const float* q_scale, const float* k_scale, const float* v_scale, void* out,
-                                  float* lse, hipStream_t s) {
+                                  const void* vt, int64_t n_tokens, const int32_t* idx, const int32_t* order,
+                                  float scale, const float* q_scale, const float* k_scale, const float* v_scale,
+                                  void* out, float* lse, hipStream_t s) {
   dim3 grid;
   int by_heads;
   if (!grid_of(L, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
@@ -1350,16 +1367,19 @@ hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& DN, const v
   auto oo = static_cast<uint16_t*>(out);
   if (L.d == 128)
     hipLaunchKernelGGL((sparse_attn_fp8_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv,
-                       vt_head_bytes, idx, scale_log2, q_scale, k_scale, v_scale, oo, lse, by_heads);
+                       vt_head_bytes, idx, idx ? order : nullptr, scale_log2, q_scale, k_scale, v_scale, oo, lse,
+                       by_heads);
   else
     hipLaunchKernelGGL((sparse_attn_fp8_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv,
-                       vt_head_bytes, idx, scale_log2, q_scale, k_scale, v_scale, oo, lse, by_heads);
+                       vt_head_bytes, idx, idx ? order : nullptr, scale_log2, q_scale, k_scale, v_scale, oo, lse,
+                       by_heads);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& DN, const void* q8, const void* k8,
-                                    const void* v, const int32_t* idx, float scale, const float* q_scale,
-                                    const float* k_scale, void* out, float* lse, hipStream_t s) {
+                                    const void* v, const int32_t* idx, const int32_t* order, float scale,
+                                    const float* q_scale, const float* k_scale, void* out, float* lse,
+                                    hipStream_t s) {
   dim3 grid;
   int by_heads;
   if (!grid_of(L, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
@@ -1370,10 +1390,10 @@ hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& DN, const
   auto oo = static_cast<uint16_t*>(out);
   if (L.d == 128)
     hipLaunchKernelGGL((sparse_attn_fp8qk_pingpong_kernel<128>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, q_scale, k_scale, oo, lse, by_heads);
+                       idx ? order : nullptr, scale_log2, q_scale, k_scale, oo, lse, by_heads);
   else
     hipLaunchKernelGGL((sparse_attn_fp8qk_pingpong_kernel<64>), grid, dim3(512), 0, s, L, DN, qq, kk, vv, idx,
-                       scale_log2, q_scale, k_scale, oo, lse, by_heads);
+                       idx ? order : nullptr, scale_log2, q_scale, k_scale, oo, lse, by_heads);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define VEDA_ABI_VERSION 5
+#define VEDA_ABI_VERSION 6
 #define VEDA_MAX_SEGMENTS 4
 #define VEDA_MAX_DENSE 8
 #define VEDA_MAX_KEY_TILES 8192   /* sum over segments of T_s accepted by selection */
@@ -206,6 +206,13 @@ int veda_select_noalloc(const veda_layer* layer, const void* q, const void* k,
  *                no key at all (all padding, no dense range) gets zero output rows.
  *                idx may be NULL when every budget[s] >= T_s: every tile of every
  *                segment is then attended (dense attention over the segments).
+ *   order      : NULL, or int32 [B, H, Tq] contiguous, 4-byte aligned (needs idx): for
+ *                every (b, h), the query tiles in the order the kernel starts them, as
+ *                veda_tile_order writes it.  Results do not depend on it; it decides
+ *                how often gathered K/V blocks are found in L2.  It should be a
+ *                permutation of 0 .. Tq-1: an entry outside that range is skipped (the
+ *                rows of a tile no entry names are not written), a tile named twice is
+ *                computed twice.  NULL is the natural order 0 .. Tq-1.
  *   dense      : host array of n_dense ranges (0 <= n_dense <= VEDA_MAX_DENSE),
  *                disjoint from the key segments and from each other.
  *   scale      : softmax scale; 0 selects 1/sqrt(d).
@@ -218,8 +225,27 @@ int veda_select_noalloc(const veda_layer* layer, const void* q, const void* k,
  * a block is partial or missing).
  */
 int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, const void* v,
-                     const int32_t* idx, const veda_range* dense, int32_t n_dense,
-                     float scale, void* out, float* lse_opt, void* stream);
+                     const int32_t* idx, const int32_t* order, const veda_range* dense,
+                     int32_t n_dense, float scale, void* out, float* lse_opt, void* stream);
+
+/*
+ * Processing order of the query tiles for the attention calls (their `order`
+ * argument).  The pages fix what the sparse execution kernel computes per query tile
+ * (Affine launch article, "Training the Selector, Not the Generator"), not the order
+ * in which tiles run; this one puts tiles whose selections start alike side by side,
+ * so that workgroups running at the same time on an XCD gather the same K/V blocks.
+ * For every (b, h): the query tiles sorted by their index rows, lexicographically, on
+ * the first segment (call order) with budget[s] < T_s: the segment block's first
+ * E = min(50 / bits, K_s) entries packed into a key, bits = the bit width of T_s - 1
+ * (at least 4), an entry at or after the block's first -1 taken as 2^bits - 1; equal
+ * keys by lower tile id.  Without such a segment, or with Tq > 16384, the
+ * identity order.
+ *   idx   : int32 [B, H, Tq, Ktot] as veda_score_topk writes it (device, 16-byte aligned)
+ *   order : int32 [B, H, Tq] contiguous (device, 4-byte aligned, output), a permutation
+ *           of 0 .. Tq-1 for every (b, h)
+ * One launch on `stream` (a workgroup per 256 query tiles of a (b, h)), no workspace.
+ */
+int veda_tile_order(const veda_layer* layer, const int32_t* idx, int32_t* order, void* stream);
 
 /*
  * FP8 variant of veda_sparse_attn's first product (row f4 of the scope: the pages'
@@ -238,8 +264,8 @@ int veda_sparse_attn(const veda_layer* layer, const void* q, const void* k, cons
  */
 int veda_sparse_attn_fp8qk(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const void* v,
                            const float* q_scale, const float* k_scale, const int32_t* idx,
-                           const veda_range* dense, int32_t n_dense, float scale, void* out,
-                           float* lse_opt, void* stream);
+                           const int32_t* order, const veda_range* dense, int32_t n_dense, float scale,
+                           void* out, float* lse_opt, void* stream);
 
 /*
  * Per-tensor FP8 quantisation for veda_sparse_attn_fp8qk: x is a bf16 tensor
@@ -279,8 +305,8 @@ int veda_quantize_fp8_e4m3(const veda_layer* layer, const void* x, uint8_t* x8, 
  */
 int veda_sparse_attn_fp8(const veda_layer* layer, const uint8_t* q8, const uint8_t* k8, const uint8_t* vt,
                          const float* q_scale, const float* k_scale, const float* v_scale,
-                         const int32_t* idx, const veda_range* dense, int32_t n_dense, float scale,
-                         void* out, float* lse_opt, void* stream);
+                         const int32_t* idx, const int32_t* order, const veda_range* dense,
+                         int32_t n_dense, float scale, void* out, float* lse_opt, void* stream);
 
 /*
  * V for veda_sparse_attn_fp8: v bf16 [B, n_tokens, H, d] (layer strides, 16-byte
@@ -304,15 +330,16 @@ size_t veda_fp8_vt_bytes(const veda_layer* layer);
  * are not needed).  No device call.
  */
 int veda_sparse_attn_check(const veda_layer* layer, const void* q, const void* k, const void* v,
-                           const int32_t* idx, const veda_range* dense, int32_t n_dense,
-                           float scale, const void* out);
+                           const int32_t* idx, const int32_t* order, const veda_range* dense,
+                           int32_t n_dense, float scale, const void* out);
 
 /*
  * One full attention layer as the video model runs it (Veda R2VA record, first
  * paragraph: the video queries use the selected reference and video tiles; text,
  * VLM conditioning and audio attention stay dense):
  *   1. veda_select for the query segment (the generated video)  -> idx;
- *   2. veda_sparse_attn for the query segment's rows;
+ *   2. veda_tile_order into the workspace (free after step 1), then veda_sparse_attn
+ *      for the query segment's rows in that order;
  *   3. for each of the n_dense_queries ranges (text, VLM, audio or reference query
  *      rows), dense attention over every token of every key segment and every
  *      dense key range, written at those rows of `out`.

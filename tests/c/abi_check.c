@@ -62,12 +62,16 @@ int main(void) {
   expect("veda_select without q", veda_select(&L, NULL, fake, fake, fake, fake, NULL, fake, 1u << 30, NULL),
          VEDA_EINVAL);
   expect("veda_sparse_attn with a dense range overlapping the video",
-         veda_sparse_attn(&L, fake, fake, fake, fake, (veda_range[]){{128000, 2000}}, 1, 0.0f, fake, NULL, NULL),
+         veda_sparse_attn(&L, fake, fake, fake, fake, NULL, (veda_range[]){{128000, 2000}}, 1, 0.0f, fake, NULL,
+                          NULL),
          VEDA_ERANGE);
   expect("veda_sparse_attn with a negative scale",
-         veda_sparse_attn(&L, fake, fake, fake, fake, dense, 2, -1.0f, fake, NULL, NULL), VEDA_EINVAL);
+         veda_sparse_attn(&L, fake, fake, fake, fake, NULL, dense, 2, -1.0f, fake, NULL, NULL), VEDA_EINVAL);
+  expect("veda_sparse_attn with an order but no index",
+         veda_sparse_attn(&L, fake, fake, fake, NULL, fake, dense, 2, 0.0f, fake, NULL, NULL), VEDA_EINVAL);
+  expect("veda_tile_order without an index", veda_tile_order(&L, NULL, fake, NULL), VEDA_EINVAL);
   expect("veda_sparse_attn_fp8qk without scales",
-         veda_sparse_attn_fp8qk(&L, fake, fake, fake, NULL, NULL, fake, dense, 2, 0.0f, fake, NULL, NULL),
+         veda_sparse_attn_fp8qk(&L, fake, fake, fake, NULL, NULL, fake, NULL, dense, 2, 0.0f, fake, NULL, NULL),
          VEDA_EINVAL);
   expect("veda_dequant_fp8_e4m3 of nothing is a no-op", veda_dequant_fp8_e4m3(fake, fake, 0, 0, NULL), VEDA_OK);
   return failures;

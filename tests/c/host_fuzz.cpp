@@ -233,11 +233,14 @@ void fuzz_layer(Rng& r, const veda_layer& L, int64_t room) {
     void* out = arg(r, 14, &bad);
     const int32_t* idx = r.chance(20) ? nullptr : static_cast<const int32_t*>(arg(r, 15, &bad));
     float* lse = r.chance(50) ? nullptr : static_cast<float*>(dev(16, r.chance(3) ? 4 : 0));
-    const int chk = veda_sparse_attn_check(&L, q, k, v, idx, dp, nd, scale, out);
+    // a processing order: absent, aligned, or 2-byte aligned (rejected); with or without idx
+    const int32_t* ord = r.chance(2) ? nullptr : static_cast<const int32_t*>(dev(22, r.chance(4) ? 2 : 0));
+    const int chk = veda_sparse_attn_check(&L, q, k, v, idx, ord, dp, nd, scale, out);
+    if (ord && !idx && !bad && c0 == VEDA_OK) EXPECT(chk == VEDA_EINVAL, "veda_sparse_attn_check order", chk);
     EXPECT(chk <= 0, "veda_sparse_attn_check", chk);
     if (c0 != VEDA_OK) EXPECT(chk == c0, "veda_sparse_attn_check", chk);
     Call c(L);
-    int st = veda_sparse_attn(&L, q, k, v, idx, dp, nd, scale, out, lse, nullptr);
+    int st = veda_sparse_attn(&L, q, k, v, idx, ord, dp, nd, scale, out, lse, nullptr);
     check_status("veda_sparse_attn", st, c);
     if (chk != VEDA_OK) EXPECT(st == chk, "veda_sparse_attn", st);
     if (st == VEDA_OK) EXPECT(c.launched() == (empty_q ? 0 : 1), "veda_sparse_attn", st);
@@ -245,7 +248,7 @@ void fuzz_layer(Rng& r, const veda_layer& L, int64_t room) {
     const float* qs = static_cast<const float*>(dev(17, r.chance(3) ? 2 : 0));
     Call c2(L);
     st = veda_sparse_attn_fp8qk(&L, static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), v,
-                                r.chance(2) ? nullptr : qs, qs, idx, dp, nd, scale, out, lse, nullptr);
+                                r.chance(2) ? nullptr : qs, qs, idx, ord, dp, nd, scale, out, lse, nullptr);
     check_status("veda_sparse_attn_fp8qk", st, c2);
     if (chk != VEDA_OK) EXPECT(st == chk, "veda_sparse_attn_fp8qk", st);
 
@@ -257,8 +260,8 @@ void fuzz_layer(Rng& r, const veda_layer& L, int64_t room) {
     // the FP8-V form: the fp8qk checks plus 64-aligned segment and dense starts
     Call c8(L);
     st = veda_sparse_attn_fp8(&L, static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
-                              static_cast<const uint8_t*>(v), qs, qs, r.chance(2) ? nullptr : qs, idx, dp, nd,
-                              scale, out, lse, nullptr);
+                              static_cast<const uint8_t*>(v), qs, qs, r.chance(2) ? nullptr : qs, idx, ord, dp,
+                              nd, scale, out, lse, nullptr);
     check_status("veda_sparse_attn_fp8", st, c8);
     if (chk != VEDA_OK) EXPECT(st == chk, "veda_sparse_attn_fp8", st);
 

@@ -133,17 +133,20 @@ hipError_t launch_score_topk(const LayerDev& L, const float* q_hat, const float*
 }
 
 hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& D, const void* q, const void* k,
-                              const void* v, const int32_t* idx, float scale, void* out, float* lse,
-                              hipStream_t) {
+                              const void* v, const int32_t* idx, const int32_t* order, float scale, void* out,
+                              float* lse, hipStream_t) {
   check_attn(L, D, q, k, v, idx, scale, out, lse, __func__);
+  REQUIRE(!order || (idx && aligned(order, 4)));
   REQUIRE(aligned(q, 16) && aligned(k, 16));
   return done();
 }
 
 hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& D, const void* q8, const void* k8,
-                                    const void* v, const int32_t* idx, float scale, const float* q_scale,
-                                    const float* k_scale, void* out, float* lse, hipStream_t) {
+                                    const void* v, const int32_t* idx, const int32_t* order, float scale,
+                                    const float* q_scale, const float* k_scale, void* out, float* lse,
+                                    hipStream_t) {
   check_attn(L, D, q8, k8, v, idx, scale, out, lse, __func__);
+  REQUIRE(!order || (idx && aligned(order, 4)));
   REQUIRE(L.tile == 128 && stub::fits);
   REQUIRE(L.sb % 16 == 0 && L.sn % 16 == 0 && L.sh % 16 == 0);
   REQUIRE(q_scale && k_scale && aligned(q_scale, 4) && aligned(k_scale, 4));
@@ -151,10 +154,11 @@ hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& D, const 
 }
 
 hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& D, const void* q8, const void* k8,
-                                  const void* vt, int64_t n_tokens, const int32_t* idx, float scale,
-                                  const float* q_scale, const float* k_scale, const float* v_scale, void* out,
-                                  float* lse, hipStream_t) {
+                                  const void* vt, int64_t n_tokens, const int32_t* idx, const int32_t* order,
+                                  float scale, const float* q_scale, const float* k_scale, const float* v_scale,
+                                  void* out, float* lse, hipStream_t) {
   check_attn(L, D, q8, k8, vt, idx, scale, out, lse, __func__);
+  REQUIRE(!order || (idx && aligned(order, 4)));
   REQUIRE(L.tile == 128 && stub::fits);
   REQUIRE(n_tokens == stub::n_tokens);
   REQUIRE(L.sb % 16 == 0 && L.sn % 16 == 0 && L.sh % 16 == 0);
@@ -169,6 +173,12 @@ hipError_t launch_quantize_fp8_vt(const LayerDev& L, int64_t n_tokens, const voi
   check_layer(L, __func__, false);
   REQUIRE(n_tokens == stub::n_tokens);
   REQUIRE(v && vt && scale && aligned(v, 16) && aligned(vt, 16) && aligned(scale, 4));
+  return done();
+}
+
+hipError_t launch_tile_order(const LayerDev& L, const int32_t* idx, int32_t* order, hipStream_t) {
+  check_layer(L, __func__);
+  REQUIRE(L.Tq >= 1 && idx && order && aligned(idx, 16) && aligned(order, 4));
   return done();
 }
 

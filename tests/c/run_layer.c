@@ -70,7 +70,7 @@ int main(int argc, char** argv) {
     fprintf(stderr, "veda_select: %s\n", veda_status_string(st));
     return 6;
   }
-  st = veda_sparse_attn(&L, q, k, v, (const int32_t*)idx, dense, n_dense, 0.0f, out, NULL, NULL);
+  st = veda_sparse_attn(&L, q, k, v, (const int32_t*)idx, NULL, dense, n_dense, 0.0f, out, NULL, NULL);
   if (st != VEDA_OK) {
     fprintf(stderr, "veda_sparse_attn: %s\n", veda_status_string(st));
     return 7;

@@ -69,3 +69,33 @@ def check_attn(out_gpu: np.ndarray, out_ref: np.ndarray):
     assert mx <= ATTN_MAX_ABS, f"max-abs {mx:.3e}"
     assert mean <= ATTN_MEAN_ABS, f"mean-abs {mean:.3e}"
     return mx, mean
+
+
+def tile_order_ref(idx: np.ndarray, seg_T, seg_K, cap: int = 16384) -> np.ndarray:
+    """The processing order veda_tile_order documents, written out plainly: per (b, h), the
+    query tiles sorted by (key, tile id), the key packing the first E entries of the first
+    segment block with K_s < T_s (bits = width of T_s - 1, at least 4; E = min(50 // bits, K_s); an entry
+    at or after the block's first -1 counts as all ones).  Identity without such a segment
+    or beyond `cap` query tiles."""
+    B, H, Tq, _ = idx.shape
+    seg = next((s for s, (T, K) in enumerate(zip(seg_T, seg_K)) if K < T), None)
+    ident = np.broadcast_to(np.arange(Tq, dtype=np.int32), (B, H, Tq)).copy()
+    if seg is None or Tq > cap:
+        return ident
+    T, K = seg_T[seg], seg_K[seg]
+    koff = sum(seg_K[:seg])
+    bits = max(4, (T - 1).bit_length())
+    nent = min(50 // bits, K)
+    out = np.empty((B, H, Tq), np.int32)
+    for b in range(B):
+        for h in range(H):
+            keys = []
+            for i in range(Tq):
+                key, ended = 0, False
+                for e in range(nent):
+                    t = int(idx[b, h, i, koff + e])
+                    ended = ended or t < 0
+                    key = (key << bits) | ((1 << bits) - 1 if ended else t)
+                keys.append((key, i))
+            out[b, h] = [i for _, i in sorted(keys)]
+    return out

@@ -37,7 +37,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert Bnd.abi_version() == 5 == Bnd.ABI_VERSION
+    assert Bnd.abi_version() == 6 == Bnd.ABI_VERSION
     for code in range(-8, 1):
         assert Bnd.status_string(code) and "unknown" not in Bnd.status_string(code)
     assert "unknown" in Bnd.status_string(-99)
@@ -143,24 +143,24 @@ def test_entry_points_reject_before_device_calls():
     assert lib.veda_select(ctypes.byref(L), fake, fake, fake, fake, fake, None, odd, need, None) == -1
     # attention: dense range overlapping a key segment, dense ranges overlapping each other
     arr, n = Bnd.dense_ranges([(133000, 100)])
-    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -4
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, None, arr, n, 0.0, fake, None, None) == -4
     arr, n = Bnd.dense_ranges([(133100, 100), (133150, 10)])
-    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -4
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, None, arr, n, 0.0, fake, None, None) == -4
     arr, n = Bnd.dense_ranges([(134800, 100)])  # past the end
-    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -4
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, None, arr, n, 0.0, fake, None, None) == -4
     # too many dense ranges
     arr, n = Bnd.dense_ranges([(133056 + i, 1) for i in range(9)])
-    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, n, 0.0, fake, None, None) == -2
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, None, arr, n, 0.0, fake, None, None) == -2
     # no keys at all: every budget zero and no dense range
     L0 = _layer()
     L0.budget[0] = 0
     L0.budget[1] = 0
     arr, n = Bnd.dense_ranges([])
-    assert lib.veda_sparse_attn(ctypes.byref(L0), fake, fake, fake, None, arr, 0, 0.0, fake, None, None) == -5
+    assert lib.veda_sparse_attn(ctypes.byref(L0), fake, fake, fake, None, None, arr, 0, 0.0, fake, None, None) == -5
     # negative or non-finite scale
     arr, n = Bnd.dense_ranges([])
-    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, 0, -1.0, fake, None, None) == -1
-    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, 0, float("nan"), fake, None, None) == -1
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, None, arr, 0, -1.0, fake, None, None) == -1
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, None, arr, 0, float("nan"), fake, None, None) == -1
     # dequant argument checks
     assert lib.veda_dequant_fp8_e4m3(fake, fake, -1, 0, None) == -1
     assert lib.veda_dequant_fp8_e4m3(None, fake, 8, 0, None) == -1
@@ -175,7 +175,7 @@ def test_empty_query_segment_is_a_no_op():
     L.query.len = 0
     fake = ctypes.c_void_p(0x10000)
     arr, n = Bnd.dense_ranges([])
-    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, arr, 0, 0.0, fake, None, None) == 0
+    assert lib.veda_sparse_attn(ctypes.byref(L), fake, fake, fake, fake, None, arr, 0, 0.0, fake, None, None) == 0
     assert lib.veda_score_topk(ctypes.byref(L), fake, fake, fake, None, None) == 0
 
 
@@ -200,12 +200,28 @@ def test_layer_attn_and_attention_checks_before_device_calls():
     assert lib.veda_layer_attn(ctypes.byref(L), fake, fake, None, fake, fake, dense, nd, dq, nq, 0.0,
                                fake, fake, fake, need, None) == -1
     # attention without an index needs every budget to cover its segment
-    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, None, dense, nd, 0.0, fake) == -1
+    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, None, None, dense, nd, 0.0, fake) == -1
     Lf = _layer()
     Lf.budget[0] = 32
     Lf.budget[1] = 1008
-    assert lib.veda_sparse_attn_check(ctypes.byref(Lf), fake, fake, fake, None, dense, nd, 0.0, fake) == 0
-    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, fake, dense, nd, 0.0, fake) == 0
+    assert lib.veda_sparse_attn_check(ctypes.byref(Lf), fake, fake, fake, None, None, dense, nd, 0.0, fake) == 0
+    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, fake, None, dense, nd, 0.0, fake) == 0
+    # a processing order needs an index and 4-byte alignment
+    assert lib.veda_sparse_attn_check(ctypes.byref(Lf), fake, fake, fake, None, fake, dense, nd, 0.0, fake) == -1
+    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, fake, ctypes.c_void_p(0x10002), dense, nd,
+                                      0.0, fake) == -1
+    assert lib.veda_sparse_attn_check(ctypes.byref(L), fake, fake, fake, fake, fake, dense, nd, 0.0, fake) == 0
+    assert lib.veda_sparse_attn(ctypes.byref(Lf), fake, fake, fake, None, fake, dense, nd, 0.0, fake, None,
+                                None) == -1
+    # veda_tile_order: null or misaligned pointers, an invalid layer; an empty query segment is a no-op
+    assert lib.veda_tile_order(ctypes.byref(L), None, fake, None) == -1
+    assert lib.veda_tile_order(ctypes.byref(L), fake, None, None) == -1
+    assert lib.veda_tile_order(ctypes.byref(L), ctypes.c_void_p(0x10008), fake, None) == -1
+    assert lib.veda_tile_order(ctypes.byref(L), fake, ctypes.c_void_p(0x10001), None) == -1
+    assert lib.veda_tile_order(None, fake, fake, None) < 0
+    Le = _layer()
+    Le.query.len = 0
+    assert lib.veda_tile_order(ctypes.byref(Le), fake, fake, None) == 0
 
 
 def _window_layer(L, tile=64, n_seg=1):
@@ -300,7 +316,7 @@ def test_fp8_entry_points_reject_before_device_calls():
     L = _layer()
     fake = ctypes.c_void_p(0x10000)
     dense, nd = Bnd.dense_ranges([(133056, 512), (133568, 256), (133824, 1024)])
-    args = lambda qs, ks: (ctypes.byref(L), fake, fake, fake, qs, ks, fake, dense, nd, 0.0, fake, None, None)
+    args = lambda qs, ks: (ctypes.byref(L), fake, fake, fake, qs, ks, fake, None, dense, nd, 0.0, fake, None, None)
     # missing or misaligned scales
     assert lib.veda_sparse_attn_fp8qk(*args(None, fake)) == -1
     assert lib.veda_sparse_attn_fp8qk(*args(fake, ctypes.c_void_p(0x10002))) == -1
@@ -316,7 +332,7 @@ def test_fp8_entry_points_reject_before_device_calls():
     Lb = Bnd.layer_from_workload(wl)
     Lb.budget[0] = 4096                          # every tile: 5482 + 40 blocks per query tile
     big, nb = Bnd.dense_ranges([(r.start, r.length) for r in wl.dense])
-    assert lib.veda_sparse_attn_fp8qk(ctypes.byref(Lb), fake, fake, fake, fake, fake, fake, big, nb, 0.0, fake,
+    assert lib.veda_sparse_attn_fp8qk(ctypes.byref(Lb), fake, fake, fake, fake, fake, fake, None, big, nb, 0.0, fake,
                                       None, None) == -2
     # quantiser: null pointers, misaligned codes or scale
     L = _layer()
@@ -340,7 +356,7 @@ def test_fp8_v_entry_points_reject_before_device_calls():
     dense, nd = Bnd.dense_ranges([(133056, 512), (133568, 256), (133824, 1024)])
 
     def call(layer, qs=fake, ks=fake, vs=fake, dn=dense, n=nd):
-        return lib.veda_sparse_attn_fp8(ctypes.byref(layer), fake, fake, fake, qs, ks, vs, fake, dn, n, 0.0, fake,
+        return lib.veda_sparse_attn_fp8(ctypes.byref(layer), fake, fake, fake, qs, ks, vs, fake, None, dn, n, 0.0, fake,
                                         None, None)
     # missing or misaligned scales
     assert call(L, vs=None) == -1

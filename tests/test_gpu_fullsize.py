@@ -2,8 +2,10 @@
 
 * Selection: the GPU selects the whole layer; the oracle selects every head as well,
   and scores and index sets are compared on every row of every head.
-* Attention fed the oracle's indices: sampled (head, query tile) pairs (first tile,
-  last tile, a tile that straddles a frame boundary, random ones) on several heads.
+* Attention fed the oracle's indices, in the processing order veda_tile_order gives them
+  (equal to its definition; the output bit-identical to the natural order's): sampled
+  (head, query tile) pairs (first tile, last tile, a tile that straddles a frame
+  boundary, random ones) on several heads.
 * The full-layer call (video rows sparse, every other query row dense over all keys):
   the call's own index sets equal the selection's; sampled video tiles and sampled
   windows of every dense query range (first and last rows, range boundaries) are
@@ -22,7 +24,7 @@ from block_sparse_attention_predictor_amd import binding as Bnd
 from block_sparse_attention_predictor_amd import inputs as I
 from oracle import veda_oracle as O
 
-from gpu_util import check_attn, check_indices, check_scores, to_dev, to_dev_bf16
+from gpu_util import check_attn, check_indices, check_scores, tile_order_ref, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -131,10 +133,18 @@ def test_selection_every_head(layer):
     print(f"[{wl.name}] selection ok on {wl.B * wl.H} heads x {wl.n_query_tiles} rows: "
           f"score error {worst:.2e}, {ties} rows decided inside the tie window", flush=True)
 
-    # attention with the oracle's indices (every head's), sampled pairs
+    # attention with the oracle's indices (every head's) in the processing order the benchmark
+    # uses (checked against its definition), sampled pairs; the natural order gives the same bits
     rng = np.random.default_rng(wl.index)
-    out = Bnd.sparse_attn(x.L, x.qd, x.kd, x.vd, to_dev(idx_ref), x.dense)
+    idx_dev = to_dev(idx_ref)
+    order = Bnd.tile_order(x.L, idx_dev)
     torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), tile_order_ref(idx_ref, x.seg_T, x.seg_K))
+    out = Bnd.sparse_attn(x.L, x.qd, x.kd, x.vd, idx_dev, x.dense, order=order)
+    out_natural = Bnd.sparse_attn(x.L, x.qd, x.kd, x.vd, idx_dev, x.dense)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_natural)
+    del out_natural
     pairs = [(0, h, t) for h in sampled_heads(wl, rng) for t in sampled_tiles(wl, rng)]
     print(f"[{wl.name}] oracle attention on {len(pairs)} (head, tile) pairs", flush=True)
     mx, mean = compare_tiles(x, out, idx_ref, pairs)
