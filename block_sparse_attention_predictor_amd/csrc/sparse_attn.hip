@@ -5,7 +5,9 @@
 // first paragraph: the selected reference and video tiles are attended per
 // query tile and head, while text, VLM conditioning and audio stay dense.
 //
-// One workgroup computes one (b, h, query tile), or two 64-row tiles.  Keys stream
+// One workgroup computes one (b, h, query tile), or two 64-row tiles, taken in the
+// caller's processing order of the query tiles when one is given (work_order.hip), else
+// in tile order; the results do not depend on it.  Keys stream
 // through LDS in blocks of 64 tokens (32 for 64-row tiles): first the tiles named by the
 // index row (gathered by id), then every dense range, cut into blocks.  The kernels
 // share the math below:
@@ -1047,17 +1049,18 @@ __device__ __forceinline__ void pingpong_attn(
 #pragma unroll
             for (int e = 0; e < 16; ++e)
               pb[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mb][e], scale_log2, -m_run));
-          float bs = 0.f;
+          // four independent sums (one chain of PC * 4 dependent dot products is slower)
+          float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
 #pragma unroll
           for (int c = 0; c < PC; ++c) {
             const bf16x2 p01 = {pb[c][0], pb[c][1]}, p23 = {pb[c][2], pb[c][3]};
             const bf16x2 p45 = {pb[c][4], pb[c][5]}, p67 = {pb[c][6], pb[c][7]};
-            bs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, bs, false);
-            bs = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, bs, false);
-            bs = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, bs, false);
-            bs = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, bs, false);
+            b0 = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, b0, false);
+            b1 = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, b1, false);
+            b2 = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, b2, false);
+            b3 = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, b3, false);
           }
-          return bs;
+          return (b0 + b1) + (b2 + b3);
         };
         if constexpr (V8) {
           // Weights are kept against the running maximum while no exponent exceeds kW8Lazy;
