@@ -142,11 +142,11 @@ class Layer:
         self.B.select(self.L, self.qd, self.kd, self.wq, self.wk, workspace=self.ws, idx=self.idx)
         self.B.tile_order(self.L, self.idx, out=self.order)
 
-    def attn(self, idx=None, L=None):
-        """Attention over the selection in its processing order, or over other index sets
-        (natural order)."""
+    def attn(self, idx=None, L=None, order=None):
+        """Attention over the selection in its processing order, or over other index sets (in
+        the order given, else the natural one)."""
         self.B.sparse_attn(L or self.L, self.qd, self.kd, self.vd, self.idx if idx is None else idx,
-                           self.dense, out=self.out, order=self.order if idx is None else None)
+                           self.dense, out=self.out, order=self.order if idx is None else order)
 
     def step(self):
         self.select()
@@ -415,16 +415,17 @@ def measure_patterns(lay, kernel_reps, log):
             B.select(Lk, lay.qd, lay.kd, lay.wq, lay.wk, workspace=ws, idx=idx)
 
         sel()
+        order = B.tile_order(Lk, idx)           # the step's configuration: the selection's tile order
         torch.cuda.synchronize()
         log(f"[{wl.name}] budget {k}")
         s_ms, _, _ = time_events(sel, kernel_reps)
-        a_ms, _, _ = time_events(lambda: lay.attn(idx, Lk), kernel_reps)
+        a_ms, _, _ = time_events(lambda: lay.attn(idx, Lk, order), kernel_reps)
         fl = lay.actual_flops(idx.cpu().numpy(), [min(k, wl.seg_tiles(sg)) for sg in wl.segments])
         out[f"budget_{k}"] = {"selector_ms": round(s_ms, 4), "attn_ms": round(a_ms, 4),
                               "density": round(fl / flops_dense, 4),
                               "actual_tflops_attn": round(fl / (a_ms * 1e-3) / 1e12, 1),
                               "recall": recall_of(Lk, idx)}
-        del idx, ws
+        del idx, ws, order
     video = [s for s in wl.segments if s.name == "video"]
     if len(wl.segments) == 1 and video and video[0].start == wl.query.start \
             and video[0].length == wl.query.length:
@@ -452,7 +453,8 @@ def measure_patterns(lay, kernel_reps, log):
 
 
 def random_pattern(lay, kernel_reps, log):
-    """Uniformly random index sets of the same budgets: the worst case for K/V reuse."""
+    """Uniformly random index sets of the same budgets, in the natural tile order: the worst
+    case for K/V reuse."""
     import torch
     wl = lay.wl
     idx = torch.from_numpy(lay.I.random_indices(wl)).to(lay.qd.device)

@@ -177,7 +177,8 @@ def test_fp8qk_full_budget_rows_batches_and_heads():
 
 def test_fp8qk_t2v5s_sampled_rows():
     """The 1344x768 5.17 s layer as the benchmark runs it: GPU quantisation of the whole Q
-    and K, GPU selection, FP8 attention of every video row; the oracle checks the scales,
+    and K, GPU selection, FP8 attention of every video row in the selection's tile order;
+    the oracle checks the scales,
     the codes of the sampled rows and the attention of sampled (head, query tile) pairs."""
     _need_gpu()
     wl = I.WORKLOADS["t2v5s"]
@@ -190,7 +191,7 @@ def test_fp8qk_t2v5s_sampled_rows():
     dense = [(r.start, r.length) for r in wl.dense]
     idx = Bnd.select(L, qd, kd, to_dev_bf16(w.wq), to_dev_bf16(w.wk))
     q8, qs, k8, ks = (*Bnd.quantize_fp8(L, qd), *Bnd.quantize_fp8(L, kd))
-    out = Bnd.sparse_attn_fp8qk(L, q8, k8, vd, qs, ks, idx, dense)
+    out = Bnd.sparse_attn_fp8qk(L, q8, k8, vd, qs, ks, idx, dense, order=Bnd.tile_order(L, idx))
     torch.cuda.synchronize()
     print("[t2v5s fp8] oracle", flush=True)
     # Q2 over the whole tensors: |x| as bf16 magnitude bits orders like the values

@@ -287,7 +287,8 @@ def test_fp8v_rejects_unaligned_starts():
 
 def test_fp8v_t2v5s_sampled_rows():
     """The 1344x768 5.17 s layer as the benchmark runs it: GPU quantisation of Q, K and V,
-    GPU selection, FP8 attention of every video row; the oracle checks the scales, the
+    GPU selection, FP8 attention of every video row in the selection's tile order; the
+    oracle checks the scales, the
     codes the sampled rows read and the attention of sampled (head, query tile) pairs."""
     _need_gpu()
     wl = I.WORKLOADS["t2v5s"]
@@ -302,7 +303,8 @@ def test_fp8v_t2v5s_sampled_rows():
     q8, qs = Bnd.quantize_fp8(L, qd)
     k8, ks = Bnd.quantize_fp8(L, kd)
     vt, vs = Bnd.quantize_fp8_vt(L, vd)
-    out, lse = Bnd.sparse_attn_fp8(L, q8, k8, vt, qs, ks, vs, idx, dense, want_lse=True)
+    out, lse = Bnd.sparse_attn_fp8(L, q8, k8, vt, qs, ks, vs, idx, dense, want_lse=True,
+                                   order=Bnd.tile_order(L, idx))
     torch.cuda.synchronize()
     print("[t2v5s fp8v] oracle", flush=True)
     exps = []
