@@ -632,9 +632,8 @@ __device__ __forceinline__ void pingpong_attn(
       qv[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): Q is in registers before any DMA is issued
-
   // wave s (s < number of streams) builds stream s's table; a stream without a tile has none
+  // (its index-row loads go out while Q's are still in flight)
   if (tid < (T2 ? 128 : 64)) {
     const int st = tid >> 6;
     const int qts = tile_of(T2 ? 2 * it + st : it);
@@ -646,6 +645,7 @@ __device__ __forceinline__ void pingpong_attn(
     if (lane == 0) snblk[st] = n;
   }
   __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): Q is in registers before any DMA is issued
   const int nblk = __builtin_amdgcn_readfirstlane(snblk[half]);
   // slots: every wave runs as many as the longer stream needs (the barriers are shared)
   const int nmax = T2 ? __builtin_amdgcn_readfirstlane(max(snblk[0], snblk[1])) : nblk;
