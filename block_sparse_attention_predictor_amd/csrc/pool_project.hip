@@ -8,11 +8,12 @@
 //
 // HBM-bound: every Q row of the query segment and every K row of the key
 // segments is read exactly once (2 * H * d bytes per token).  One workgroup
-// owns one tile and a group of 8 heads; its 256 threads stream the tile's rows
-// with 16-byte loads (d/8 lanes per head row, 8 heads side by side, so a wave
-// reads whole contiguous head rows), sum in fp32 registers, combine the
-// row-parallel partial sums through LDS, divide by the number of real tokens,
-// then apply W[h] (bf16 or f16, read through L2, converted exactly) with fp32 dot
+// owns four tiles of one kind and a group of 8 heads; for each tile its 256
+// threads stream the rows with 16-byte loads (d/8 lanes per head row, 8 heads side
+// by side, so a wave reads whole contiguous head rows; eight rows in flight per
+// thread), sum in fp32 registers, combine the row-parallel partial sums through
+// LDS and divide by the number of real tokens.  Then W[h] (bf16 or f16, read
+// through L2 once for the four tiles, converted exactly) is applied with fp32 dot
 // products.
 #include "common.h"
 
@@ -38,6 +39,9 @@ __device__ __forceinline__ float whi(uint32_t w) {
   else return bf16hi(w);
 }
 
+// Tiles of one kind (query or key) per workgroup: each W row is read once for all of them.
+constexpr int kTilesPerGroup = 4;
+
 template <int D, bool F16>
 __global__ __launch_bounds__(kThreads) void pool_project_kernel(
     LayerDev L, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -46,92 +50,89 @@ __global__ __launch_bounds__(kThreads) void pool_project_kernel(
   constexpr int TPR = D / 8;                               // lanes per head row
   constexpr int RP = kThreads / (kHeadsPerGroup * TPR);    // token rows in flight per step
   __shared__ float red[RP][kHeadsPerGroup * D];
+  __shared__ float means[kTilesPerGroup][kHeadsPerGroup * D];
 
-  const int job = blockIdx.x;
+  const int qgroups = (L.Tq + kTilesPerGroup - 1) / kTilesPerGroup;
+  const bool is_q = (int)blockIdx.x < qgroups;
+  const int first = (is_q ? (int)blockIdx.x : (int)blockIdx.x - qgroups) * kTilesPerGroup;
+  const int total = is_q ? L.Tq : L.Tk;
+  const int ntiles = min(kTilesPerGroup, total - first);
+  const uint16_t* const x = is_q ? q : k;
+  const uint16_t* const W = is_q ? wq : wk;
+  float* const out = is_q ? q_hat : k_hat;
   const int h0 = blockIdx.y * kHeadsPerGroup;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-
-  // which tile: query tiles first, then the key tiles of every segment in call order
-  const uint16_t* x;
-  const uint16_t* W;
-  float* out;
-  int64_t start, len;
-  int64_t row_out;   // tile index within q_hat or k_hat
-  int32_t T_out;
-  if (job < L.Tq) {
-    x = q;
-    W = wq;
-    out = q_hat;
-    start = L.q0 + (int64_t)job * L.tile;
-    len = min((int64_t)L.tile, L.qlen - (int64_t)job * L.tile);
-    row_out = job;
-    T_out = L.Tq;
-  } else {
-    const int j = job - L.Tq;
-    int s = 0;
-#pragma unroll
-    for (int t = 1; t < kMaxSeg; ++t)
-      if (t < L.n_seg && j >= L.seg[t].toff) s = t;
-    const int tl = j - L.seg[s].toff;
-    x = k;
-    W = wk;
-    out = k_hat;
-    start = L.seg[s].start + (int64_t)tl * L.tile;
-    len = min((int64_t)L.tile, L.seg[s].len - (int64_t)tl * L.tile);
-    row_out = j;
-    T_out = L.Tk;
-  }
-
   const int hl = (tid / TPR) % kHeadsPerGroup;
   const int r0 = tid / (TPR * kHeadsPerGroup);
   const int c = (tid % TPR) * 8;
   const int h = h0 + hl;
   const bool hv = h < L.H;
 
-  float acc[8];
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int j = first + tt;                   // tile index within q_hat or k_hat
+    int64_t start, len;
+    if (is_q) {
+      start = L.q0 + (int64_t)j * L.tile;
+      len = min((int64_t)L.tile, L.qlen - (int64_t)j * L.tile);
+    } else {
+      int s = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-
-  if (hv) {
-    const uint16_t* base = x + (int64_t)b * L.sb + start * L.sn + (int64_t)h * L.sh + c;
-    int64_t r = r0;
-    // four rows in flight per thread
-    for (; r + 3 * RP < len; r += 4 * RP) {
-      u32x4 v[4];
+      for (int t = 1; t < kMaxSeg; ++t)
+        if (t < L.n_seg && j >= L.seg[t].toff) s = t;
+      const int tl = j - L.seg[s].toff;
+      start = L.seg[s].start + (int64_t)tl * L.tile;
+      len = min((int64_t)L.tile, L.seg[s].len - (int64_t)tl * L.tile);
+    }
+    float acc[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (r + u * RP) * L.sn));
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (hv) {
+      const uint16_t* base = x + (int64_t)b * L.sb + start * L.sn + (int64_t)h * L.sh + c;
+      int64_t r = r0;
+      // eight rows in flight per thread
+      for (; r + 7 * RP < len; r += 8 * RP) {
+        u32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc[0] += bf16lo(v[u].x); acc[1] += bf16hi(v[u].x);
-        acc[2] += bf16lo(v[u].y); acc[3] += bf16hi(v[u].y);
-        acc[4] += bf16lo(v[u].z); acc[5] += bf16hi(v[u].z);
-        acc[6] += bf16lo(v[u].w); acc[7] += bf16hi(v[u].w);
+        for (int u = 0; u < 8; ++u)
+          v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (r + u * RP) * L.sn));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          acc[0] += bf16lo(v[u].x); acc[1] += bf16hi(v[u].x);
+          acc[2] += bf16lo(v[u].y); acc[3] += bf16hi(v[u].y);
+          acc[4] += bf16lo(v[u].z); acc[5] += bf16hi(v[u].z);
+          acc[6] += bf16lo(v[u].w); acc[7] += bf16hi(v[u].w);
+        }
+      }
+      for (; r < len; r += RP) {
+        u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + r * L.sn));
+        acc[0] += bf16lo(v.x); acc[1] += bf16hi(v.x);
+        acc[2] += bf16lo(v.y); acc[3] += bf16hi(v.y);
+        acc[4] += bf16lo(v.z); acc[5] += bf16hi(v.z);
+        acc[6] += bf16lo(v.w); acc[7] += bf16hi(v.w);
       }
     }
-    for (; r < len; r += RP) {
-      u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + r * L.sn));
-      acc[0] += bf16lo(v.x); acc[1] += bf16hi(v.x);
-      acc[2] += bf16lo(v.y); acc[3] += bf16hi(v.y);
-      acc[4] += bf16lo(v.z); acc[5] += bf16hi(v.z);
-      acc[6] += bf16lo(v.w); acc[7] += bf16hi(v.w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[r0][hl * D + c + e] = acc[e];
+    __syncthreads();
+    // combine the row-parallel partial sums; mean over the real tokens
+    const float inv_len = 1.0f / (float)len;
+    for (int i = tid; i < kHeadsPerGroup * D; i += kThreads) {
+      float s = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RP; ++rr) s += red[rr][i];
+      means[tt][i] = s * inv_len;
     }
+    __syncthreads();
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[r0][hl * D + c + e] = acc[e];
-  __syncthreads();
-  // combine the row-parallel partial sums; mean over the real tokens
-  const float inv_len = 1.0f / (float)len;
-  for (int i = tid; i < kHeadsPerGroup * D; i += kThreads) {
-    float s = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < RP; ++rr) s += red[rr][i];
-    red[0][i] = s * inv_len;
+  // the last workgroup of a kind may have fewer tiles: their slots hold zeros
+  if (ntiles < kTilesPerGroup) {
+    float* const spare = &means[0][0] + ntiles * kHeadsPerGroup * D;
+    for (int i = tid; i < (kTilesPerGroup - ntiles) * kHeadsPerGroup * D; i += kThreads) spare[i] = 0.f;
+    __syncthreads();
   }
-  __syncthreads();
 
-  // projection: x_hat[h, o] = sum_c W[h, o, c] * mean[h, c]
+  // projection: x_hat[h, o] = sum_c W[h, o, c] * mean[h, c], each W row read once for the tiles
   const int P = L.p;
   for (int o = tid; o < kHeadsPerGroup * P; o += kThreads) {
     const int ohl = o / P;
@@ -139,18 +140,24 @@ __global__ __launch_bounds__(kThreads) void pool_project_kernel(
     const int oh = h0 + ohl;
     if (oh >= L.H) continue;
     const uint4* wrow = reinterpret_cast<const uint4*>(W + ((int64_t)oh * P + oc) * D);
-    const float* m = &red[0][ohl * D];
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll 4
+    float s0[kTilesPerGroup], s1[kTilesPerGroup];
+#pragma unroll
+    for (int tt = 0; tt < kTilesPerGroup; ++tt) s0[tt] = s1[tt] = 0.f;
+#pragma unroll 2
     for (int cc = 0; cc < D / 8; ++cc) {
       const uint4 w = wrow[cc];
-      const float* mm = m + cc * 8;
-      s0 = fmaf(wlo<F16>(w.x), mm[0], s0); s1 = fmaf(whi<F16>(w.x), mm[1], s1);
-      s0 = fmaf(wlo<F16>(w.y), mm[2], s0); s1 = fmaf(whi<F16>(w.y), mm[3], s1);
-      s0 = fmaf(wlo<F16>(w.z), mm[4], s0); s1 = fmaf(whi<F16>(w.z), mm[5], s1);
-      s0 = fmaf(wlo<F16>(w.w), mm[6], s0); s1 = fmaf(whi<F16>(w.w), mm[7], s1);
+#pragma unroll
+      for (int tt = 0; tt < kTilesPerGroup; ++tt) {
+        const float* mm = &means[tt][ohl * D + cc * 8];
+        s0[tt] = fmaf(wlo<F16>(w.x), mm[0], s0[tt]); s1[tt] = fmaf(whi<F16>(w.x), mm[1], s1[tt]);
+        s0[tt] = fmaf(wlo<F16>(w.y), mm[2], s0[tt]); s1[tt] = fmaf(whi<F16>(w.y), mm[3], s1[tt]);
+        s0[tt] = fmaf(wlo<F16>(w.z), mm[4], s0[tt]); s1[tt] = fmaf(whi<F16>(w.z), mm[5], s1[tt]);
+        s0[tt] = fmaf(wlo<F16>(w.w), mm[6], s0[tt]); s1[tt] = fmaf(whi<F16>(w.w), mm[7], s1[tt]);
+      }
     }
-    out[(((int64_t)b * L.H + oh) * T_out + row_out) * P + oc] = s0 + s1;
+#pragma unroll
+    for (int tt = 0; tt < kTilesPerGroup; ++tt)
+      if (tt < ntiles) out[(((int64_t)b * L.H + oh) * total + first + tt) * P + oc] = s0[tt] + s1[tt];
   }
 }
 
@@ -158,8 +165,8 @@ __global__ __launch_bounds__(kThreads) void pool_project_kernel(
 
 hipError_t launch_pool_project(const LayerDev& L, const void* q, const void* k, const void* wq,
                                const void* wk, float* q_hat, float* k_hat, hipStream_t s) {
-  dim3 grid((unsigned)(L.Tq + L.Tk), (unsigned)((L.H + kHeadsPerGroup - 1) / kHeadsPerGroup),
-            (unsigned)L.B);
+  dim3 grid((unsigned)((L.Tq + kTilesPerGroup - 1) / kTilesPerGroup + (L.Tk + kTilesPerGroup - 1) / kTilesPerGroup),
+            (unsigned)((L.H + kHeadsPerGroup - 1) / kHeadsPerGroup), (unsigned)L.B);
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto wqq = static_cast<const uint16_t*>(wq);
