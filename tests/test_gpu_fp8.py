@@ -90,6 +90,30 @@ def test_quantize_codes_and_scale(d, head_major):
         assert np.array_equal(_codes(c8), codes_ref), shift        # scaling by 2^s changes no code
 
 
+@pytest.mark.parametrize("k", [0, 3, -5])
+def test_quantize_every_bf16_value_in_range(k):
+    """Every finite bf16 value with |x| <= 448 * 2^k, once each (largest first, so the scale
+    is 2^k): the codes equal the oracle's nearest-even rounding, ties and the subnormal
+    codes included."""
+    _need_gpu()
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0 * 2.0 ** k)
+    b16 = bits[keep].astype(np.uint16)
+    b16 = b16[np.argsort(-np.abs(vals[keep]), kind="stable")]
+    n = -(-b16.size // 256) * 256
+    flat = np.zeros(n, np.uint16)
+    flat[:b16.size] = b16
+    x = flat.reshape(1, n // 256, 2, 128)
+    dev = to_dev_bf16(x)
+    L = _layer_for(x.shape, tuple(dev.stride()[:3]))
+    c8, sc = Bnd.quantize_fp8(L, dev)
+    torch.cuda.synchronize()
+    codes_ref, e_ref = O.quantize_fp8(x)
+    assert e_ref == k and float(sc.cpu()[0]) == 2.0 ** k
+    assert np.array_equal(_codes(c8), codes_ref)
+
+
 def test_quantize_all_zero_and_signed_zero():
     _need_gpu()
     B, N, H, d = 1, 64, 2, 64
