@@ -683,11 +683,31 @@ __device__ __forceinline__ void pingpong_attn(
   // compiler's wait-count pass does not see it: it would otherwise wait for every LDS
   // DMA in flight before each LDS operand read.  All waits for these loads are explicit
   // (s_waitcnt vmcnt) and ordered by the workgroup barriers.
-  auto dma1 = [](const char* g, uint32_t off, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_addr), "v"(off), "s"(g)
-                 : "memory", "m0");
+  // NL such loads fill consecutive 1 KB LDS slots from lds_addr; one asm block steps M0
+  // by 1 KB between them, so that no per-load address has to stay in a scalar register.
+  auto dma_n = [](auto nl, const char* g, const uint32_t (&o)[4], uint32_t lds_addr) {
+    constexpr int NL = decltype(nl)::value;
+    static_assert(NL == 1 || NL == 2 || NL == 4, "loads per block and thread");
+    if constexpr (NL == 1) {
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(lds_addr), "v"(o[0]), "s"(g)
+                   : "memory", "m0");
+    } else if constexpr (NL == 2) {
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3\n\t"
+                   "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
+                   :
+                   : "s"(lds_addr), "v"(o[0]), "v"(o[1]), "s"(g)
+                   : "memory", "m0", "scc");
+    } else {
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5\n\t"
+                   "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %5\n\t"
+                   "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %5\n\t"
+                   "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %5"
+                   :
+                   : "s"(lds_addr), "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "s"(g)
+                   : "memory", "m0", "scc");
+    }
   };
   // a block's K (IS_V = 0) or V (IS_V = 1) rows; rows past a partial block's end load
   // its last row again
@@ -699,13 +719,10 @@ __device__ __forceinline__ void pingpong_attn(
     constexpr bool BLOCKED = IS_V && V8;        // FP8 V: the 64-token block of the first key
     const char* g = BLOCKED ? base + (blk.start >> 6) * (int64_t)(D * 64) : base + blk.start * L.sn * EB;
     const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t)(reinterpret_cast<char*>(dst) + wsi * NL * 1024);
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
     if (BLOCKED || blk.n == KBK) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        uint32_t o = off[i];
-        asm volatile("" : "+v"(o));
-        dma1(g, o, l0 + i * 1024);
-      }
+      for (int i = 0; i < NL; ++i) o[i] = off[i];
     } else {
       int ln = lane;
       asm volatile("" : "+v"(ln) : : "memory");
@@ -713,9 +730,10 @@ __device__ __forceinline__ void pingpong_attn(
       for (int i = 0; i < NL; ++i) {
         const int r = ((wsi * NL + i) * 64 + ln) / CP;
         const int rc = r < blk.n ? r : blk.n - 1;
-        dma1(g, off[i] - (uint32_t)((r - rc) * (int)L.sn * EB), l0 + i * 1024);
+        o[i] = off[i] - (uint32_t)((r - rc) * (int)L.sn * EB);
       }
     }
+    dma_n(std::integral_constant<int, NL>{}, g, o, l0);
   };
   const std::integral_constant<bool, false> kK{};
   const std::integral_constant<bool, true> kV{};
