@@ -632,6 +632,16 @@ __device__ __forceinline__ void pingpong_attn(
       qv[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  // A products slot with no previous block multiplies P = 0 by a V stage: both V stages of
+  // each stream start zeroed, so that a stage no DMA has filled yet holds finite values.
+  // The stores are 1 KB stripes that cross the slices the stream's waves later fill by
+  // LDS DMA, so they go before the workgroup barrier below: no wave issues a DMA into a
+  // stage while another wave's zero stores to it may still be pending.
+  {
+    uint4* const z = reinterpret_cast<uint4*>((grp ? sg1 : sg0) + half * 4 * KBK * D + 2 * KBK * D);
+#pragma unroll
+    for (int i = 0; i < 2 * KBK * D * 2 / 16 / TS; ++i) z[i * TS + (tid & (TS - 1))] = make_uint4(0, 0, 0, 0);
+  }
   // wave s (s < number of streams) builds stream s's table; a stream without a tile has none
   // (its index-row loads go out while Q's are still in flight)
   if (tid < (T2 ? 128 : 64)) {
@@ -813,14 +823,6 @@ __device__ __forceinline__ void pingpong_attn(
         asm volatile("" : "+v"(vB[part]));
       }
     }
-    // A products slot with no previous block multiplies P = 0 by a V stage: both stages
-    // start zeroed so that a stage no DMA has filled yet holds finite values.
-    {
-      uint4* z = reinterpret_cast<uint4*>(Vs0);
-#pragma unroll
-      for (int i = 0; i < 2 * KBK * D * 2 / 16 / TS; ++i) z[i * TS + (tid & (TS - 1))] = make_uint4(0, 0, 0, 0);
-    }
-
     // this group's j-th block c_j is block 2j + GRP of the table; K(c_j) and V(c_j)
     // live in stage j % 2
     auto entry = [&](int i) {
@@ -840,7 +842,6 @@ __device__ __forceinline__ void pingpong_attn(
       np = LPT;
     }
     wait_vm(np);                              // K(c_0) and K(c_1) landed
-    __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the zeroed V stages are written
     barrier();
     if (GRP) {                                // group 1 runs one slot behind
       barrier();
