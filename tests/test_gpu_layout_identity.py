@@ -8,9 +8,10 @@ all three outputs must agree bit for bit.  A difference is a race: an LDS stage 
 by ordinary stores while another wave's LDS DMA into it is in flight, or an operand read
 before its DMA landed.  Such races need the skew between waves that full-size memory
 traffic brings, which the small determinism layers do not reach, so these run at the
-benchmark's sizes: the 90 %-sparsity layer (mid: paired 64-row kernel) and the 5.17 s
-layer (t2v5s: two-group bf16 kernel and both FP8 kernels), in the selection's tile order
-as the benchmark runs them.
+benchmark's sizes: the 90 %-sparsity layer (mid: paired 64-row kernel), the 5.17 s
+layer (t2v5s: two-group bf16 kernel and both FP8 kernels) and the R2VA layer (two-group
+kernel over two selected segments, the reference one taken whole by every tile), in the
+selection's tile order as the benchmark runs them.
 """
 import gc
 
@@ -45,7 +46,7 @@ def _side_stream(fn):
     return out
 
 
-@pytest.mark.parametrize("name", ["mid", "t2v5s"])
+@pytest.mark.parametrize("name", ["mid", "t2v5s", "r2va"])
 def test_attention_bits_independent_of_layout_and_timing(name):
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a GPU")
