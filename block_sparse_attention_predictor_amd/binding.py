@@ -260,6 +260,18 @@ def select_workspace_bytes(layer: Layer) -> int:
     return _load().veda_select_workspace_bytes(ctypes.byref(layer))
 
 
+def _workspace(workspace, nbytes: int, device):
+    """The caller's workspace, checked: a contiguous tensor on `device` of at least nbytes
+    bytes (the kernels write q_hat and k_hat there and cannot detect a smaller buffer).
+    None gives a new one."""
+    if workspace is None:
+        return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    if workspace.device != device or not workspace.is_contiguous() or \
+            workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a contiguous tensor on {device} of at least {nbytes} bytes")
+    return workspace
+
+
 def project(layer: Layer, q, k, wq, wk, stream=None):
     """Pooled + projected vectors (q_hat [B,H,Tq,p], k_hat [B,H,Tk,p], fp32)."""
     _check_qkv(layer, q, k)
@@ -303,8 +315,7 @@ def select(layer: Layer, q, k, wq, wk, want_scores: bool = False, workspace=None
     nbytes = select_workspace_bytes(layer)
     if nbytes == 0:
         _check(_load().veda_layer_check(ctypes.byref(layer), 1), "veda_select")
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     st = _load().veda_select(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(idx),
                              _ptr(sc), _ptr(workspace), nbytes, _stream(stream))
     _check(st, "veda_select")
@@ -504,8 +515,7 @@ def layer_attn(layer: Layer, q, k, v, wq, wk, dense: Sequence[Tuple[int, int]] =
     nbytes = select_workspace_bytes(layer)
     if nbytes == 0:
         _check(_load().veda_layer_check(ctypes.byref(layer), 1), "veda_layer_attn")
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     darr, nd = dense_ranges(list(dense))
     qarr, nq = dense_ranges(list(dense_queries))
     st = _load().veda_layer_attn(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk),

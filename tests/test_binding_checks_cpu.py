@@ -72,3 +72,18 @@ def test_two_group_merge_area_fits_its_buffer(D):
     slot = w * (D // 32) * 4 * 64 + (db * 4 + e4) * 64 + l
     assert slot.min() == 0 and slot.max() < sg0_float4
     assert np.unique(slot).size == slot.size
+
+
+def test_workspace_size_contiguity_and_device():
+    cpu = torch.device("cpu")
+    ws = B._workspace(None, 1000, cpu)
+    assert ws.dtype == torch.uint8 and ws.numel() >= 1000
+    good = torch.empty(1000, dtype=torch.uint8)
+    assert B._workspace(good, 1000, cpu) is good
+    assert B._workspace(torch.empty(250, dtype=torch.float32), 1000, cpu).numel() == 250   # bytes, not elements
+    with pytest.raises(ValueError):
+        B._workspace(torch.empty(999, dtype=torch.uint8), 1000, cpu)
+    with pytest.raises(ValueError):
+        B._workspace(torch.empty(2000, dtype=torch.uint8)[::2], 1000, cpu)
+    with pytest.raises(ValueError):
+        B._workspace(good, 1000, torch.device("meta"))
