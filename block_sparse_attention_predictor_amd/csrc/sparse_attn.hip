@@ -141,9 +141,12 @@ __device__ __forceinline__ int swz_v(int row) { return (row & 3) * (CPR / 4); }
 //    a contiguous slice of its query tiles.  The head's K/V (tens of MB) then stays in the
 //    shared Infinity Cache while it is in use, and neighbouring query tiles, whose
 //    selections overlap, share each XCD's L2.
-//  * by heads (no index: every tile of every segment, e.g. the dense query rows of a
-//    layer): every XCD takes whole heads, so the query tiles of one head, which read the
-//    same keys in the same order, run side by side and share that XCD's L2.
+//  * by heads: every XCD takes whole heads, so the query tiles of one head run side by
+//    side and share that XCD's L2, and no other XCD fetches that head's keys.  Mode 1
+//    (no index: every tile of every segment, e.g. the dense query rows of a layer) runs
+//    a head's tiles in tile order; mode 2 (index rows given, and the K/V of the eight
+//    heads in flight small enough to stay in the Infinity Cache together) runs them in
+//    the caller's processing order.
 // n is the number of work items per (b, h): query tiles, or pairs of them.
 // Returns false for a padding workgroup (a uniform exit before any barrier).
 __device__ __forceinline__ bool work_item(const LayerDev& L, int n, int by_heads, int& bh, int& it) {
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(64 * NW, KBK == 32 ? 4 : 2) void sparse_attn_kernel
 
   int bh, qt;
   if (!work_item(L, by_heads, bh, qt)) return;     // padding workgroup (uniform exit)
-  if (!by_heads && (qt = tile_at(L, order, bh, qt)) < 0) return;   // no tile at this position
+  if (by_heads != 1 && (qt = tile_at(L, order, bh, qt)) < 0) return;   // no tile at this position
   const int h = bh % L.H;
   const int b = bh / L.H;
 
@@ -600,7 +603,7 @@ __device__ __forceinline__ void pingpong_attn(
   if (!work_item(L, T2 ? (L.Tq + 1) >> 1 : L.Tq, by_heads, bh, it)) return;   // padding workgroup
   const int h = bh % L.H;
   const int b = bh / L.H;
-  auto tile_of = [&](int pos) { return by_heads ? (pos < L.Tq ? pos : -1) : tile_at(L, order, bh, pos); };
+  auto tile_of = [&](int pos) { return by_heads == 1 ? (pos < L.Tq ? pos : -1) : tile_at(L, order, bh, pos); };
   const int qt_at = tile_of(T2 ? 2 * it + half : it);
   if (!T2 && qt_at < 0) return;                   // uniform over the workgroup
   const bool tile_ok = qt_at >= 0;
@@ -1312,8 +1315,15 @@ bool table_fits(const LayerDev& L, const DenseDev& DN, int kbk, int64_t cap) {
 }
 
 // grid of n work items per (b, h), in work_item's XCD-aware order
-bool grid_of(const LayerDev& L, int64_t n, const int32_t* idx, dim3& grid, int& by_heads) {
-  by_heads = idx == nullptr && L.B * L.H >= 8;
+// by_heads: 0 by tiles, 1 by heads in tile order, 2 by heads in the caller's order (eight
+// heads' K and V, 2 * 2 bytes * d per key token each, within 160 MB of the 256 MB
+// Infinity Cache; larger layers keep every XCD on one head so that its keys stay there)
+bool grid_of(const LayerDev& L, const DenseDev& DN, int64_t n, const int32_t* idx, dim3& grid, int& by_heads) {
+  int64_t keys = 0;
+  for (int i = 0; i < L.n_seg; ++i) keys += L.seg[i].len;
+  for (int i = 0; i < DN.n; ++i) keys += DN.r[i].len;
+  const bool fits = (int64_t)8 * 2 * keys * L.d * 2 <= ((int64_t)160 << 20);
+  by_heads = L.B * L.H < 8 ? 0 : idx == nullptr ? 1 : fits ? 2 : 0;
   const int64_t per_xcd = (n + 7) / 8;
   const int64_t nwork = by_heads ? ((int64_t)L.B * L.H + 7) / 8 * 8 * n : (int64_t)L.B * L.H * per_xcd * 8;
   if (nwork > 0x7FFFFFFF) return false;
@@ -1340,7 +1350,7 @@ hipError_t launch_sparse_attn(const LayerDev& L, const DenseDev& DN, const void*
   const bool pair = pair_fits(L, DN);
   dim3 grid;
   int by_heads;
-  if (!grid_of(L, pair ? ((int64_t)L.Tq + 1) / 2 : L.Tq, idx, grid, by_heads)) return hipErrorInvalidValue;
+  if (!grid_of(L, DN, pair ? ((int64_t)L.Tq + 1) / 2 : L.Tq, idx, grid, by_heads)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
   const int32_t* const ord = idx ? order : nullptr;
   auto qq = static_cast<const uint16_t*>(q);
@@ -1380,7 +1390,7 @@ hipError_t launch_sparse_attn_fp8(const LayerDev& L, const DenseDev& DN, const v
                                   void* out, float* lse, hipStream_t s) {
   dim3 grid;
   int by_heads;
-  if (!grid_of(L, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
+  if (!grid_of(L, DN, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
   const int64_t vt_head_bytes = (n_tokens + 63) / 64 * (int64_t)L.d * 64;
   auto qq = static_cast<const uint8_t*>(q8);
@@ -1404,7 +1414,7 @@ hipError_t launch_sparse_attn_fp8qk(const LayerDev& L, const DenseDev& DN, const
                                     hipStream_t s) {
   dim3 grid;
   int by_heads;
-  if (!grid_of(L, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
+  if (!grid_of(L, DN, L.Tq, idx, grid, by_heads) || !two_group_fits(L, DN)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.44269504088896340736f;
   auto qq = static_cast<const uint8_t*>(q8);
   auto kk = static_cast<const uint8_t*>(k8);
