@@ -242,10 +242,9 @@ def device_peaks(log):
 
 
 def environment():
-    """Device, software versions and the GPU clock levels rocm-smi reports once the timed work is
-    over (the idle levels; the clock under sustained MFMA load is not sampled here)."""
+    """Device and software versions.  No other program is started from this process once it
+    has used the GPU; the clock under load comes from the hardware counters in profiles/."""
     import platform
-    import subprocess
     import torch
     p = torch.cuda.get_device_properties(0)
     env = {"device": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
@@ -255,12 +254,6 @@ def environment():
         env["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:
         env["rocm"] = None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
-        env["clocks_after_run"] = [ln.split(":", 1)[1].strip() for ln in r.stdout.splitlines()
-                                   if "clk" in ln.lower() and "level" in ln.lower()]
-    except (OSError, subprocess.SubprocessError):
-        env["clocks_after_run"] = None
     return env
 
 
