@@ -11,6 +11,8 @@
   table) and both FP8 kernels.
 * An order entry outside [0, Tq) is skipped: the rows of the tile no entry names keep
   their previous contents, every other tile is as in the natural order.
+* Small indexed layers run whole heads per XCD in the caller's order: oracle parity on
+  every tile with padding head slots and an odd tile count, for both 128- and 64-row tiles.
 """
 import numpy as np
 import pytest
@@ -202,3 +204,40 @@ def test_order_entries_outside_the_tiles_are_skipped(tile):
             r0, r1 = t * tile, min((t + 1) * tile, query[1])
             want = sentinel if (h, t) in skipped else ref
             assert torch.equal(out[0, r0:r1, h], want[0, r0:r1, h]), (h, t)
+
+
+@pytest.mark.parametrize("tile", [128, 64])
+def test_whole_heads_per_xcd_matches_oracle(tile):
+    """Indexed layers whose eight heads' K and V fit the Infinity Cache together run whole
+    heads per XCD, in the caller's order.  Here B * H = 10, so the grid's last head slots
+    are padding workgroups, and 9 query tiles (the last one partial), so at tile 64 the last
+    paired workgroup has one tile; every tile is compared with the oracle, in the sorted
+    order and in the natural one."""
+    _need_gpu()
+    from block_sparse_attention_predictor_amd import inputs as I
+    from oracle import veda_oracle as O
+    from gpu_util import bf16_to_f64, check_attn
+    g = np.random.default_rng(23)
+    B, H, d = 2, 5, 64
+    qlen = 9 * tile - 17
+    segs = [(0, qlen, 3)]
+    dense = [(qlen, 70)]
+    query = (0, qlen)
+    N = qlen + 70
+    Tq = -(-qlen // tile)
+    idx = _rows(g, B, H, Tq, segs, tile, pad_every=4)
+    q, k, v = (I.f32_to_bf16_bits(g.standard_normal((B, N, H, d)).astype(np.float32)) for _ in range(3))
+    L = _layer(B, H, d, tile, N, query, segs)
+    qd, kd, vd = (to_dev_bf16(x) for x in (q, k, v))
+    idx_dev = to_dev(idx)
+    order = Bnd.tile_order(L, idx_dev)
+    out = Bnd.sparse_attn(L, qd, kd, vd, idx_dev, dense, order=order)
+    nat = Bnd.sparse_attn(L, qd, kd, vd, idx_dev, dense)
+    torch.cuda.synchronize()
+    assert torch.equal(out, nat)
+    o = bf16_to_f64(out)
+    res = O.attend(q, k, v, idx, tile, query, segs, dense)
+    assert len(res) == B * H * Tq
+    for (b, h, i), (ref, _) in res.items():
+        r0, r1 = i * tile, min((i + 1) * tile, qlen)
+        check_attn(o[b, r0:r1, h], ref)
